@@ -1,0 +1,18 @@
+"""CPU oracle for draft-tree verification (test infrastructure only).
+
+A plain, slow, float64 numpy statement of what the verify step computes. Only the tests,
+the smoke check and the benchmark's CPU-baseline leg may import it; the HIP library and
+its binding never do, and this package imports nothing from them.
+"""
+
+from .tree_verify import (  # noqa: F401
+    accept,
+    anc_bitmask_words,
+    argmax_rows,
+    bf16_bits_to_f64,
+    tree_attention,
+    tree_structure,
+    validate_parent,
+    verify,
+    visibility_mask,
+)
