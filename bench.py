@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark: one tree-verify step on the 128K-context, 64-node workload, one GPU.
+
+Workload (synthetic, seeded): KV length 131072 + 64 tree rows, 32 q heads / 8 KV heads,
+head dim 128, bf16 N(0,1); a 64-node random tree of depth <= 16; logits [64, 152064]
+bf16 with a planted path. One step = 64 back-to-back layer-equivalent tree-attention
+calls, each on its own KV buffer (64 buffers, 34.4 GB, far beyond the 256 MB Infinity
+Cache), then one argmax over the logits and one acceptance walk.
+
+Reported ``value``: microseconds per tree-verify call = mean attention time per
+layer-equivalent call + argmax time + acceptance time (HIP events on the stream the
+kernels run on). ``roofline`` relates the attention call's algorithmic bytes (K + V + Q +
+out) to its measured duration against the 8 TB/s HBM peak. ``cpu_baseline`` times the
+float64 CPU oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-check]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+LAYERS = 64
+WORKLOAD = "long_128k"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-check", action="store_true", help="skip the parity re-check")
+    ap.add_argument("--layers", type=int, default=LAYERS)
+    ap.add_argument("--splits", type=int, default=0, help="force the KV split count (0 = library choice)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: the verify step is measured per device "
+              "(multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import draft_tree_verification_tv_amd as tv
+    from workloads import make
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tv.lib()
+
+    log("generating the seeded workload (CPU)")
+    w = make(WORKLOAD, 0)
+    N, L, Hq, Hkv, D, V = w.N, w.L, w.Hq, w.Hkv, w.D, w.V
+    T = L + N
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    layers = args.layers
+    log(f"allocating {layers} KV buffers ({2 * layers * T * Hkv * D * 2 / 1e9:.1f} GB)")
+    K = torch.empty((layers, T, Hkv, D), dtype=torch.bfloat16, device=dev)
+    Vc = torch.empty((layers, T, Hkv, D), dtype=torch.bfloat16, device=dev)
+    K[0].copy_(to_dev(w.k))
+    Vc[0].copy_(to_dev(w.v))
+    g = torch.Generator(device=dev)
+    g.manual_seed(42)
+    for b in range(1, layers):
+        K[b].normal_(generator=g)
+        Vc[b].normal_(generator=g)
+    q = to_dev(w.q)
+    parent = torch.from_numpy(w.parent).to(dev)
+    draft = torch.from_numpy(w.draft).to(dev)
+    logits = to_dev(w.logits)
+    out = torch.empty((N, Hq, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(tv.tree_attn_workspace_size(N, L, Hq, Hkv, D, args.splits), dtype=torch.uint8, device=dev)
+    am_ws = tv.argmax_workspace(N, V, dev)
+    tok = torch.empty(N, dtype=torch.int32, device=dev)
+    acc = (torch.empty(1, dtype=torch.int32, device=dev), torch.empty(N, dtype=torch.int32, device=dev),
+           torch.empty(N, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev))
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        for b in range(layers):
+            tv.tree_attn(q, K[b], Vc[b], parent, L=L, scale=w.scale, num_splits=args.splits, out=out, workspace=ws,
+                         stream=stream)
+        if ev:
+            ev[1].record(stream)
+        tv.argmax(logits, tok=tok, workspace=am_ws, stream=stream)
+        if ev:
+            ev[2].record(stream)
+        tv.accept(parent, draft, tok, out=acc, stream=stream)
+        if ev:
+            ev[3].record(stream)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    attn_ms = np.array([e[0].elapsed_time(e[1]) for e in events]) / layers
+    argmax_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    accept_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in events])
+    t_attn_us = float(np.median(attn_ms) * 1e3)
+    t_argmax_us = float(np.median(argmax_ms) * 1e3)
+    t_accept_us = float(np.median(accept_ms) * 1e3)
+    call_us = t_attn_us + t_argmax_us + t_accept_us
+    ms_per_step = wall * 1e3 / args.steps
+
+    kv_bytes = 2 * T * Hkv * D * 2
+    qo_bytes = 2 * N * Hq * D * 2
+    algo_bytes = kv_bytes + qo_bytes
+    achieved = algo_bytes / (t_attn_us * 1e-6) / 1e9
+    kv_gbps = kv_bytes / (t_attn_us * 1e-6) / 1e9
+    log(f"attn {t_attn_us:.1f} us/call ({kv_gbps:.0f} GB/s KV, {kv_gbps / HBM_PEAK_GBS:.1%} of peak), "
+        f"argmax {t_argmax_us:.1f} us, accept {t_accept_us:.1f} us, step {ms_per_step:.2f} ms")
+
+    parity = None
+    if not args.no_check:
+        import oracle
+        log("parity re-check on KV buffer 0 (argmax, accept, 2 q heads of attention)")
+        tv.tree_attn(q, K[0], Vc[0], parent, L=L, scale=w.scale, num_splits=args.splits, out=out, workspace=ws)
+        tv.argmax(logits, tok=tok, workspace=am_ws)
+        tv.accept(parent, draft, tok, out=acc)
+        torch.cuda.synchronize()
+        sub = [0, Hq - 1]
+        qf = oracle.bf16_bits_to_f64(w.q[:, sub])
+        kf = oracle.bf16_bits_to_f64(w.k[:, [0, Hkv - 1]])
+        vf = oracle.bf16_bits_to_f64(w.v[:, [0, Hkv - 1]])
+        ref, _ = oracle.tree_attention(qf, kf, vf, w.parent, w.scale)
+        got = out[:, sub].float().cpu().numpy().astype(np.float64)
+        err = float(np.abs(got - ref).max())
+        rel = float((np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)).max())
+        etok = oracle.argmax_rows(oracle.bf16_bits_to_f64(w.logits))
+        eln = oracle.accept(w.parent, w.draft, etok)[0]
+        parity = {"attn_max_abs": err, "attn_row_rel": rel, "argmax_exact": bool((tok.cpu().numpy() == etok).all()),
+                  "accept_exact": int(acc[0].item()) == eln, "accept_len": eln}
+        ok = err <= 1e-2 and rel <= 2e-2 and parity["argmax_exact"] and parity["accept_exact"]
+        log(f"parity {'OK' if ok else 'FAILED'}: {parity}")
+        if not ok:
+            sys.exit(1)
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        log(f"CPU oracle baseline: one layer call on 1 of {Hkv} KV heads, plus argmax and accept ({threads} cores)")
+        G = Hq // Hkv
+        qf = oracle.bf16_bits_to_f64(w.q[:, :G])
+        kf = oracle.bf16_bits_to_f64(w.k[:, :1])
+        vf = oracle.bf16_bits_to_f64(w.v[:, :1])
+        lf = oracle.bf16_bits_to_f64(w.logits)
+        t0 = time.perf_counter()
+        oracle.tree_attention(qf, kf, vf, w.parent, w.scale)
+        t_head = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        etok = oracle.argmax_rows(lf)
+        oracle.accept(w.parent, w.draft, etok)
+        t_rest = time.perf_counter() - t0
+        cpu_us = (t_head * Hkv + t_rest) * 1e6
+        cpu = {"value": cpu_us, "unit": "us per tree-verify call", "cores": threads, "kind": "oracle",
+               "sample": f"float64 numpy oracle: tree attention of one layer call for 1 of {Hkv} KV heads "
+                         f"({G} q heads x {N} nodes x {T} keys) scaled x{Hkv}, plus argmax of the "
+                         f"[{N}, {V}] logits and the accept walk, measured once"}
+        log(f"CPU oracle: {cpu_us / 1e3:.1f} ms per call")
+
+    rec = {
+        "metric": "µs per tree-verify call (attn+argmax+accept) and KV GB/s vs HBM peak",
+        "value": round(call_us, 2),
+        "unit": "µs",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "long_128k: KV 131072 + 64-node tree (depth<=16), 32 q / 8 KV heads, D=128, "
+                               "bf16; logits [64,152064] bf16; 64 layer-equivalent attention calls on distinct "
+                               "KV buffers + argmax + accept per step",
+                   "kv_len": L, "nodes": N, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "vocab": V,
+                   "layers_per_step": layers, "parallelism": "none (1 GPU)"},
+        "breakdown_us": {"attn_per_call": round(t_attn_us, 2), "argmax": round(t_argmax_us, 2),
+                         "accept": round(t_accept_us, 2), "attn_p10": round(float(np.percentile(attn_ms, 10) * 1e3), 2),
+                         "attn_p90": round(float(np.percentile(attn_ms, 90) * 1e3), 2)},
+        "kv_gbps": round(kv_gbps, 1),
+        "kv_hbm_frac": round(kv_gbps / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "tv_tree_attn (split + merge)", "algorithmic_bytes": algo_bytes},
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

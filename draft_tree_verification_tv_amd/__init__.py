@@ -1,0 +1,24 @@
+"""Tree verification for speculative decoding on AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libtv.so`` (hand-written HIP, C ABI in ``include/tv.h``); this
+package is its thin Python binding.
+"""
+
+from .tv import (  # noqa: F401
+    EXPORTS,
+    HEAD_DIM,
+    MAX_NODES,
+    TVError,
+    abi_version,
+    accept,
+    argmax,
+    argmax_workspace,
+    argmax_workspace_size,
+    lib,
+    status_string,
+    tree_attn,
+    tree_attn_workspace_size,
+    tree_prep,
+    validate_tree_host,
+    verify,
+)

@@ -1,0 +1,62 @@
+"""Build libtv.so (HIP for gfx950) in-tree with hipcc.
+
+The library is one shared object compiled from the sources in ``csrc/``; it exports the
+C ABI declared in ``include/tv.h``. Usage: ``python -m draft_tree_verification_tv_amd.build``.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+REPO_ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(REPO_ROOT, "include")
+LIB_DIR = os.path.join(PKG_DIR, "lib")
+LIB_PATH = os.path.join(LIB_DIR, "libtv.so")
+SOURCES = ["tv_api.hip", "tv_attn.hip", "tv_argmax.hip", "tv_tree.hip"]
+ARCH = "gfx950"
+
+# Packed fp32 VALU ops are disabled for all device code: the kernels rely on plain
+# scalar fp32 arithmetic only.
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; a ROCm toolchain is required to build libtv")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into libtv.so (always recompiles). Returns its path."""
+    os.makedirs(LIB_DIR, exist_ok=True)
+    fd, tmp = tempfile.mkstemp(prefix="libtv.", suffix=".so.tmp", dir=LIB_DIR)
+    os.close(fd)
+    cmd = [hipcc(), *FLAGS, f"-I{INCLUDE}", *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    try:
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        noise = "is not a recognized feature for this target"
+        err = "\n".join(ln for ln in res.stderr.splitlines() if noise not in ln)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{err}")
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+        os.replace(tmp, LIB_PATH)
+    finally:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

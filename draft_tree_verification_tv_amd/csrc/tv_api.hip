@@ -1,0 +1,117 @@
+// C ABI of libtv: host-side validation, plans and launches. Declarations and the
+// contract of every entry point are in include/tv.h.
+//
+// A versioned ABI query and static descriptive strings follow the plugin-ABI pattern of
+// the ROCmFPX page (bittide.aicompass.dev article, "plugin system" section): a caller can
+// refuse a library whose version does not match its header.
+#include <atomic>
+#include <cmath>
+
+#include "tv_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int status_of(hipError_t e) { return e == hipSuccess ? TV_OK : TV_ERR_HIP; }
+
+bool attn_args_ok(int N, int L, int Hq, int Hkv, int num_splits) {
+  return N >= 1 && N <= TV_MAX_NODES && L >= 0 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0 &&
+         num_splits >= 0 && num_splits <= 1024 && (int64_t)L + N <= INT32_MAX - 64 &&
+         (int64_t)Hq * N <= (1 << 24);
+}
+
+}  // namespace
+
+extern "C" {
+
+int tv_abi_version(void) { return TV_ABI_VERSION; }
+
+const char* tv_status_string(int status) {
+  switch (status) {
+    case TV_OK: return "ok";
+    case TV_ERR_INVALID_ARG: return "invalid argument";
+    case TV_ERR_BAD_TREE: return "parent[] entry outside [-1, i-1]";
+    case TV_ERR_UNSUPPORTED: return "unsupported configuration (head dim must be 128)";
+    case TV_ERR_WORKSPACE: return "workspace missing or too small";
+    case TV_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int tv_validate_tree_host(const int32_t* parent_host, int N) {
+  if (!parent_host || N < 1 || N > TV_MAX_NODES) return TV_ERR_INVALID_ARG;
+  for (int i = 0; i < N; ++i)
+    if (parent_host[i] < -1 || parent_host[i] >= i) return TV_ERR_BAD_TREE;
+  return TV_OK;
+}
+
+int tv_tree_prep(const int32_t* parent, int N, uint64_t* anc, int32_t* depth, int32_t* dev_error,
+                 void* stream) {
+  if (!parent || N < 1 || N > TV_MAX_NODES) return TV_ERR_INVALID_ARG;
+  return status_of(tv::launch_tree_prep(parent, N, anc, depth, dev_error, static_cast<hipStream_t>(stream)));
+}
+
+size_t tv_tree_attn_workspace_size(int N, int L, int Hq, int Hkv, int D, int num_splits) {
+  if (!attn_args_ok(N, L, Hq, Hkv, num_splits) || D != TV_HEAD_DIM) return 0;
+  const tv::AttnPlan p = tv::attn_plan(N, L, Hq, Hkv, num_splits, cu_count());
+  return tv::attn_workspace_bytes(p, Hkv);
+}
+
+int tv_tree_attn(const void* q, const void* k, const void* v, int64_t kv_stride_t, int64_t kv_stride_h,
+                 const int32_t* parent, int N, int L, int Hq, int Hkv, int D, float scale, int num_splits,
+                 void* out, float* lse, void* workspace, size_t workspace_bytes, int32_t* dev_error,
+                 void* stream) {
+  if (!q || !k || !v || !parent || !out) return TV_ERR_INVALID_ARG;
+  if (!attn_args_ok(N, L, Hq, Hkv, num_splits)) return TV_ERR_INVALID_ARG;
+  if (D != TV_HEAD_DIM) return TV_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return TV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return TV_ERR_INVALID_ARG;
+  if (kv_stride_t < 0 || kv_stride_h < 0 || kv_stride_t % 8 || kv_stride_h % 8) return TV_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return TV_ERR_INVALID_ARG;
+  const tv::AttnPlan p = tv::attn_plan(N, L, Hq, Hkv, num_splits, cu_count());
+  const size_t need = tv::attn_workspace_bytes(p, Hkv);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return TV_ERR_WORKSPACE;
+  return status_of(tv::launch_tree_attn(p, q, k, v, kv_stride_t, kv_stride_h, parent, N, L, Hq, Hkv, scale, out,
+                                        lse, workspace, dev_error, static_cast<hipStream_t>(stream)));
+}
+
+size_t tv_argmax_workspace_size(int N, int V) {
+  if (N < 1 || V < 1 || V >= INT32_MAX) return 0;
+  return tv::argmax_workspace_bytes(N, V);
+}
+
+int tv_argmax(const void* logits, int dtype, int N, int V, int64_t row_stride, int32_t* tok, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  if (!logits || !tok) return TV_ERR_INVALID_ARG;
+  if (N < 1 || N > 65535 || V < 1 || V >= INT32_MAX || row_stride < V) return TV_ERR_INVALID_ARG;
+  if (dtype != TV_BF16 && dtype != TV_F32) return TV_ERR_INVALID_ARG;
+  const size_t need = tv::argmax_workspace_bytes(N, V);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return TV_ERR_WORKSPACE;
+  return status_of(tv::launch_argmax(logits, dtype, N, V, row_stride, tok, workspace,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int tv_accept(const int32_t* parent, const int32_t* draft, const int32_t* tok, int N, int32_t* accept_len,
+              int32_t* accept_nodes, int32_t* accept_tokens, int32_t* bonus, int32_t* dev_error, void* stream) {
+  if (!parent || !draft || !tok || !accept_len || !accept_nodes || !accept_tokens) return TV_ERR_INVALID_ARG;
+  if (N < 1 || N > TV_MAX_NODES) return TV_ERR_INVALID_ARG;
+  return status_of(tv::launch_accept(parent, draft, tok, N, accept_len, accept_nodes, accept_tokens, bonus,
+                                     dev_error, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,213 @@
+"""Python binding of libtv (ctypes): argument marshalling only.
+
+Every computation runs in the HIP kernels of ``libtv.so``; torch provides device memory
+and the current stream. There is no fallback: if the library is missing or a call fails,
+an exception is raised.
+
+Function names match the C ABI in ``include/tv.h`` without the ``tv_`` prefix.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+from .build import LIB_PATH
+
+TV_OK, TV_ERR_INVALID_ARG, TV_ERR_BAD_TREE, TV_ERR_UNSUPPORTED, TV_ERR_WORKSPACE, TV_ERR_HIP = range(6)
+TV_BF16, TV_F32 = 0, 1
+MAX_NODES = 256
+HEAD_DIM = 128
+
+EXPORTS = ("tv_abi_version", "tv_status_string", "tv_validate_tree_host", "tv_tree_prep",
+           "tv_tree_attn_workspace_size", "tv_tree_attn", "tv_argmax_workspace_size",
+           "tv_argmax", "tv_accept")
+
+
+class TVError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+_lock = threading.Lock()
+_vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+
+
+def lib():
+    """Load libtv.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m draft_tree_verification_tv_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.tv_abi_version.restype = _i32
+        L.tv_abi_version.argtypes = []
+        L.tv_status_string.restype = ctypes.c_char_p
+        L.tv_status_string.argtypes = [_i32]
+        L.tv_validate_tree_host.restype = _i32
+        L.tv_validate_tree_host.argtypes = [_vp, _i32]
+        L.tv_tree_prep.restype = _i32
+        L.tv_tree_prep.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp]
+        L.tv_tree_attn_workspace_size.restype = _sz
+        L.tv_tree_attn_workspace_size.argtypes = [_i32] * 6
+        L.tv_tree_attn.restype = _i32
+        L.tv_tree_attn.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _i32, _i32, _i32, _i32, _i32,
+                                   _f32, _i32, _vp, _vp, _vp, _sz, _vp, _vp]
+        L.tv_argmax_workspace_size.restype = _sz
+        L.tv_argmax_workspace_size.argtypes = [_i32, _i32]
+        L.tv_argmax.restype = _i32
+        L.tv_argmax.argtypes = [_vp, _i32, _i32, _i32, _i64, _vp, _vp, _sz, _vp]
+        L.tv_accept.restype = _i32
+        L.tv_accept.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
+        if L.tv_abi_version() != 1:
+            raise RuntimeError("libtv ABI version mismatch")
+        _lib = L
+        return L
+
+
+def _check(status: int, where: str):
+    if status != TV_OK:
+        raise TVError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need_cuda(name, t, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def abi_version() -> int:
+    return lib().tv_abi_version()
+
+
+def status_string(status: int) -> str:
+    return lib().tv_status_string(status).decode()
+
+
+def validate_tree_host(parent) -> int:
+    """Host check of a parent array; returns a status code (0 = valid)."""
+    p = torch.as_tensor(parent, dtype=torch.int32).contiguous().cpu()
+    return lib().tv_validate_tree_host(ctypes.c_void_p(p.data_ptr()), p.numel())
+
+
+def tree_prep(parent, dev_error=None, stream=None):
+    """Ancestor bitmasks (int64 [N, 4], bit patterns of uint64 words) and depths int32 [N]."""
+    _need_cuda("parent", parent, torch.int32)
+    n = parent.numel()
+    anc = torch.empty((n, 4), dtype=torch.int64, device=parent.device)
+    depth = torch.empty(n, dtype=torch.int32, device=parent.device)
+    _check(lib().tv_tree_prep(_ptr(parent), n, _ptr(anc), _ptr(depth), _ptr(dev_error), _stream(stream)),
+           "tv_tree_prep")
+    return anc, depth
+
+
+def tree_attn_workspace_size(N, L, Hq, Hkv, D=HEAD_DIM, num_splits=0) -> int:
+    return int(lib().tv_tree_attn_workspace_size(N, L, Hq, Hkv, D, num_splits))
+
+
+def tree_attn(q, k, v, parent, L=None, scale=None, num_splits=0, out=None, lse=None,
+              workspace=None, dev_error=None, stream=None):
+    """Tree-masked attention. q bf16 [N, Hq, D]; k, v bf16 [>= L+N, Hkv, D] (last dim
+    contiguous); parent int32 [N]. Returns out bf16 [N, Hq, D] (and fills ``lse`` fp32
+    [N, Hq] when given)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need_cuda(name, t, torch.bfloat16)
+    _need_cuda("parent", parent, torch.int32)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be 3-D")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if k.stride() != v.stride() or k.stride(2) != 1:
+        raise ValueError("k and v must share strides with a contiguous last dim")
+    N, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if L is None:
+        L = k.shape[0] - N
+    if L < 0 or k.shape[0] < L + N or v.shape[0] < L + N:
+        raise ValueError("k/v must hold L + N rows")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((N, Hq, D), dtype=torch.bfloat16, device=q.device)
+    ws_bytes = tree_attn_workspace_size(N, L, Hq, Hkv, D, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().tv_tree_attn(_ptr(q), _ptr(k), _ptr(v), k.stride(0), k.stride(1), _ptr(parent), N, L, Hq,
+                              Hkv, D, float(scale), int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _ptr(dev_error), _stream(stream)),
+           "tv_tree_attn")
+    return out
+
+
+def argmax_workspace_size(N, V) -> int:
+    return int(lib().tv_argmax_workspace_size(N, V))
+
+
+def argmax_workspace(N, V, device) -> torch.Tensor:
+    """A zero-filled argmax workspace (the kernels leave it zero-filled after each call)."""
+    return torch.zeros(max(argmax_workspace_size(N, V), 256), dtype=torch.uint8, device=device)
+
+
+def argmax(logits, tok=None, workspace=None, V=None, stream=None):
+    """Row argmax (lowest index on ties) of bf16 or fp32 logits [N, row_stride]."""
+    _need_cuda("logits", logits)
+    if logits.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("logits must be bf16 or fp32")
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be 2-D with a contiguous last dim")
+    N = logits.shape[0]
+    V = logits.shape[1] if V is None else V
+    if tok is None:
+        tok = torch.empty(N, dtype=torch.int32, device=logits.device)
+    if workspace is None:
+        workspace = argmax_workspace(N, V, logits.device)
+    dt = TV_F32 if logits.dtype == torch.float32 else TV_BF16
+    _check(lib().tv_argmax(_ptr(logits), dt, N, V, logits.stride(0), _ptr(tok), _ptr(workspace),
+                           workspace.numel(), _stream(stream)), "tv_argmax")
+    return tok
+
+
+def accept(parent, draft, tok, out=None, dev_error=None, stream=None):
+    """Longest accepted path. Returns (accept_len [1], nodes [N], tokens [N], bonus [1])."""
+    for name, t in (("parent", parent), ("draft", draft), ("tok", tok)):
+        _need_cuda(name, t, torch.int32)
+    N = parent.numel()
+    if out is None:
+        dev = parent.device
+        out = (torch.empty(1, dtype=torch.int32, device=dev), torch.empty(N, dtype=torch.int32, device=dev),
+               torch.empty(N, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev))
+    ln, nodes, toks, bonus = out
+    _check(lib().tv_accept(_ptr(parent), _ptr(draft), _ptr(tok), N, _ptr(ln), _ptr(nodes), _ptr(toks),
+                           _ptr(bonus), _ptr(dev_error), _stream(stream)), "tv_accept")
+    return ln, nodes, toks, bonus
+
+
+def verify(q, k, v, parent, logits, draft, L=None, scale=None, num_splits=0, attn_workspace=None,
+           argmax_ws=None, stream=None):
+    """One verify step: tree attention, row argmax and acceptance, all enqueued on one stream."""
+    out = tree_attn(q, k, v, parent, L=L, scale=scale, num_splits=num_splits, workspace=attn_workspace,
+                    stream=stream)
+    tok = argmax(logits, workspace=argmax_ws, stream=stream)
+    return out, tok, accept(parent, draft, tok, stream=stream)

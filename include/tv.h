@@ -1,0 +1,147 @@
+/*
+ * tv.h -- C ABI of libtv: target-side verification of a speculative draft tree on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method. A drafter proposes a block of tokens; the target model checks the whole
+ * block in one pass, keeps the tokens it agrees with and drops the rest (DFlash
+ * contributor guide, discosf.com/news/4742660, section "What is DFlash?"). With DDTree
+ * verification the block is a tree of alternative continuations that the target scores
+ * in one forward pass (Lucebox-Hub review, aichain-blog.pages.dev, section "2. DFlash";
+ * Lucebox Hub tips page, d9249.github.io/tips/lucebox-hub, section "Lucebox Hub
+ * overview"). Greedy verification compares each draft token with the target's
+ * temperature-0 sample, the argmax of its logits (DFlash contributor guide, section
+ * "Coding conventions", `sample(logits, temperature=0.0)`).
+ *
+ * This library computes the data-parallel part of one verify step:
+ *   tv_tree_prep  parent[] -> ancestor bitmasks and depths            (integer)
+ *   tv_tree_attn  tree-masked attention of N nodes over a bf16 KV cache
+ *   tv_argmax     row argmax of the target logits                      (bit exact)
+ *   tv_accept     longest accepted root-to-node path                   (bit exact)
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE pointers unless the name ends in _host. The caller owns every
+ *     buffer; the library never allocates or frees.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls only
+ *     enqueue work and never synchronise the host; results appear in stream order.
+ *   - Every call returns a tv_status. Arguments that the host can check are checked
+ *     before anything is enqueued; a failed check enqueues nothing.
+ *   - A tree is given as parent[N] (int32, device): parent[i] in [-1, i-1], -1 meaning
+ *     "child of the committed prefix". Node order is therefore topological. A kernel
+ *     that meets an entry outside that range treats it as -1 and, when `dev_error` is
+ *     non-NULL, stores TV_ERR_BAD_TREE there (it never writes TV_OK; clear it first).
+ *     tv_validate_tree_host() gives the same check synchronously on a host copy.
+ *   - No global mutable state: calls on different streams may run concurrently as
+ *     long as they do not share output or workspace buffers.
+ */
+#ifndef TV_H_
+#define TV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TV_ABI_VERSION 1
+#define TV_MAX_NODES 256   /* ancestor sets are 4 x 64-bit words */
+#define TV_HEAD_DIM 128    /* the only head dimension the kernels are built for */
+
+typedef enum {
+  TV_OK = 0,
+  TV_ERR_INVALID_ARG = 1, /* null pointer, size out of range, misaligned buffer */
+  TV_ERR_BAD_TREE = 2,    /* parent[] entry outside [-1, i-1] */
+  TV_ERR_UNSUPPORTED = 3, /* valid request the kernels are not built for (D != 128) */
+  TV_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
+  TV_ERR_HIP = 5          /* the HIP runtime refused a launch */
+} tv_status;
+
+typedef enum { TV_BF16 = 0, TV_F32 = 1 } tv_dtype;
+
+/* ABI version compiled into the library; equals TV_ABI_VERSION of a matching header. */
+int tv_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char* tv_status_string(int status);
+
+/* Synchronous host check of a parent array (host memory). TV_OK, TV_ERR_BAD_TREE, or
+ * TV_ERR_INVALID_ARG for a NULL pointer or N outside [1, TV_MAX_NODES]. */
+int tv_validate_tree_host(const int32_t* parent_host, int N);
+
+/*
+ * Tree preprocessing. For every node i:
+ *   anc[i][w]  bit j of word w is set when node 64*w + j is i or an ancestor of i
+ *              (uint64 [N][4], little-endian word order; bits >= N are zero);
+ *   depth[i]   number of nodes on the path from the prefix to i (1 for a child of the
+ *              prefix) = popcount of anc[i].
+ * Either output may be NULL (then it is not written). 1 <= N <= TV_MAX_NODES.
+ * The same routine runs inside tv_tree_attn and tv_accept; this entry point exposes it.
+ */
+int tv_tree_prep(const int32_t* parent, int N, uint64_t* anc, int32_t* depth,
+                 int32_t* dev_error, void* stream);
+
+/*
+ * Tree-masked attention (one layer's verify attention).
+ *
+ * Node i's query attends to every context key t in [0, L) and to the tree keys L + j
+ * for j = i and every ancestor j of i -- the one-pass tree forward read as masked
+ * softmax attention. Query head h reads KV head h / (Hq / Hkv).
+ *
+ *   q        bf16 [N][Hq][D], contiguous, 16-byte aligned.
+ *   k, v     bf16; element (t, kvh, d) at base + t*kv_stride_t + kvh*kv_stride_h + d
+ *            (strides in elements, multiples of 8; d contiguous; 16-byte aligned base).
+ *            Rows t in [0, L) are the context, rows L + i are tree node i's own key and
+ *            value. Only rows [0, L + N) are read.
+ *   parent   int32 [N] (see conventions).
+ *   scale    softmax scale applied to q.k (1/sqrt(D) for standard attention).
+ *   num_splits  number of KV splits per (KV head, row tile); 0 = library's choice.
+ *   out      bf16 [N][Hq][D] (round to nearest even), contiguous, 16-byte aligned.
+ *   lse      optional fp32 [N][Hq], natural-log sum of exp of the scaled scores.
+ *   workspace   device scratch of at least tv_tree_attn_workspace_size(...) bytes with
+ *               the same num_splits; 256-byte aligned. Contents need no initialisation.
+ * Limits: 1 <= N <= TV_MAX_NODES, L >= 0, D == TV_HEAD_DIM, Hkv >= 1, Hq % Hkv == 0,
+ * num_splits in [0, 1024]. Accumulation is fp32; inputs are never modified.
+ */
+size_t tv_tree_attn_workspace_size(int N, int L, int Hq, int Hkv, int D, int num_splits);
+
+int tv_tree_attn(const void* q, const void* k, const void* v, int64_t kv_stride_t,
+                 int64_t kv_stride_h, const int32_t* parent, int N, int L, int Hq,
+                 int Hkv, int D, float scale, int num_splits, void* out, float* lse,
+                 void* workspace, size_t workspace_bytes, int32_t* dev_error,
+                 void* stream);
+
+/*
+ * Row argmax: tok[i] = the lowest index u with logits[i][u] equal to the row maximum
+ * (float comparison, so -0.0 and +0.0 tie). Rows holding NaN give an unspecified index.
+ *   logits   dtype TV_BF16 or TV_F32, row i at base + i*row_stride elements.
+ *   tok      int32 [N].
+ *   workspace   at least tv_argmax_workspace_size(N, V) bytes, 256-byte aligned. It must
+ *               be zero-filled before its first use; every call leaves it zero-filled
+ *               again, so one buffer serves any number of calls on one stream.
+ * Limits: N >= 1, 1 <= V < 2^31 - 1, row_stride >= V.
+ */
+size_t tv_argmax_workspace_size(int N, int V);
+
+int tv_argmax(const void* logits, int dtype, int N, int V, int64_t row_stride,
+              int32_t* tok, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Longest accepted path. Node i matches when draft[i] == tok[i]; a node is accepted when
+ * it and all its ancestors match. The result is the longest accepted root-to-node path;
+ * among equally long paths the one ending at the lowest node index.
+ *   accept_len     int32 [1]: path length (0 when nothing is accepted).
+ *   accept_nodes   int32 [N]: path nodes root to leaf, then -1 padding.
+ *   accept_tokens  int32 [N]: draft tokens of those nodes, then -1 padding.
+ *   bonus          optional int32 [1]: tok of the lowest-index child of the path's last
+ *                  node (of the prefix when nothing is accepted), -1 if it has none.
+ * Limits: 1 <= N <= TV_MAX_NODES. Runs as a single workgroup.
+ */
+int tv_accept(const int32_t* parent, const int32_t* draft, const int32_t* tok, int N,
+              int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
+              int32_t* bonus, int32_t* dev_error, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TV_H_ */

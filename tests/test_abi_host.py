@@ -1,0 +1,133 @@
+"""Host-side checks of libtv that need no GPU: exports, versions, argument validation.
+
+Every call here is rejected (or answered) by host code before any kernel is enqueued,
+so the tests run on machines without a GPU. They need the built library.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import draft_tree_verification_tv_amd as tv
+from draft_tree_verification_tv_amd.build import LIB_PATH
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "tv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB_PATH), reason="libtv.so not built")
+
+FAKE = ctypes.c_void_p(0x10000)        # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(tv_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_documented_calls():
+    names = declared_functions()
+    for n in ("tv_tree_attn", "tv_argmax", "tv_accept", "tv_tree_prep", "tv_abi_version",
+              "tv_validate_tree_host"):
+        assert n in names
+    assert set(names) == set(tv.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported():
+    raw = ctypes.CDLL(LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(raw, n), n
+
+
+def test_version_and_strings():
+    assert tv.abi_version() == 1
+    for s in range(6):
+        assert tv.status_string(s)
+    assert tv.status_string(99) == "unknown status"
+
+
+def test_validate_tree_host():
+    assert tv.validate_tree_host([-1, 0, 1]) == 0
+    assert tv.validate_tree_host([-1, -1, 0, 2]) == 0
+    assert tv.validate_tree_host([0]) == 2
+    assert tv.validate_tree_host([-1, 1]) == 2
+    assert tv.validate_tree_host([-1, -2]) == 2
+    assert tv.validate_tree_host(np.full(257, -1)) == 1
+    L = tv.lib()
+    assert L.tv_validate_tree_host(None, 3) == 1
+
+
+def attn_call(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, st=1024, sh=128, parent=FAKE, N=4, L=100, Hq=8, Hkv=2, D=128,
+             scale=0.088, splits=0, out=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 40, err=None, stream=None)
+    a.update(kw)
+    return tv.lib().tv_tree_attn(a["q"], a["k"], a["v"], a["st"], a["sh"], a["parent"], a["N"], a["L"],
+                                 a["Hq"], a["Hkv"], a["D"], a["scale"], a["splits"], a["out"], a["lse"],
+                                 a["ws"], a["ws_bytes"], a["err"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(parent=None), 1), (dict(out=None), 1),
+    (dict(N=0), 1), (dict(N=257), 1), (dict(L=-1), 1), (dict(Hq=6, Hkv=4), 1), (dict(Hkv=0), 1),
+    (dict(D=64), 3), (dict(D=256), 3), (dict(scale=0.0), 1), (dict(scale=-1.0), 1),
+    (dict(scale=float("inf")), 1), (dict(st=1001), 1), (dict(sh=-8), 1),
+    (dict(q=ctypes.c_void_p(0x10002)), 1), (dict(splits=-1), 1), (dict(splits=5000), 1),
+    (dict(ws=None), 4), (dict(ws_bytes=16), 4), (dict(ws=ctypes.c_void_p(0x10008)), 4),
+])
+def test_tree_attn_rejects(kw, status):
+    assert attn_call(**kw) == status
+
+
+def test_workspace_sizes():
+    s = tv.tree_attn_workspace_size(64, 131072, 32, 8)
+    assert s > 0 and s % 256 == 0
+    assert tv.tree_attn_workspace_size(64, 131072, 32, 8, D=64) == 0
+    assert tv.tree_attn_workspace_size(0, 10, 32, 8) == 0
+    # a forced split count is honoured in the size (more splits, more partials)
+    assert tv.tree_attn_workspace_size(64, 8192, 32, 8, num_splits=32) > \
+        tv.tree_attn_workspace_size(64, 8192, 32, 8, num_splits=2)
+    a = tv.argmax_workspace_size(64, 152064)
+    assert a > 0 and a % 256 == 0
+    assert tv.argmax_workspace_size(0, 10) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 0, 4, 100, 100, FAKE, FAKE, 1 << 30), 1),
+    ((FAKE, 0, 4, 100, 100, None, FAKE, 1 << 30), 1),
+    ((FAKE, 2, 4, 100, 100, FAKE, FAKE, 1 << 30), 1),
+    ((FAKE, 0, 0, 100, 100, FAKE, FAKE, 1 << 30), 1),
+    ((FAKE, 0, 4, 0, 100, FAKE, FAKE, 1 << 30), 1),
+    ((FAKE, 0, 4, 100, 99, FAKE, FAKE, 1 << 30), 1),
+    ((FAKE, 0, 4, 100, 100, FAKE, None, 1 << 30), 4),
+    ((FAKE, 0, 4, 100, 100, FAKE, FAKE, 8), 4),
+])
+def test_argmax_rejects(args, status):
+    assert tv.lib().tv_argmax(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, FAKE, FAKE, 4, FAKE, FAKE, FAKE), 1),
+    ((FAKE, None, FAKE, 4, FAKE, FAKE, FAKE), 1),
+    ((FAKE, FAKE, None, 4, FAKE, FAKE, FAKE), 1),
+    ((FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE), 1),
+    ((FAKE, FAKE, FAKE, 257, FAKE, FAKE, FAKE), 1),
+    ((FAKE, FAKE, FAKE, 4, None, FAKE, FAKE), 1),
+    ((FAKE, FAKE, FAKE, 4, FAKE, None, FAKE), 1),
+    ((FAKE, FAKE, FAKE, 4, FAKE, FAKE, None), 1),
+])
+def test_accept_rejects(args, status):
+    assert tv.lib().tv_accept(*args, None, None, None) == status
+
+
+def test_tree_prep_rejects():
+    L = tv.lib()
+    assert L.tv_tree_prep(None, 4, FAKE, FAKE, None, None) == 1
+    assert L.tv_tree_prep(FAKE, 0, FAKE, FAKE, None, None) == 1
+    assert L.tv_tree_prep(FAKE, 300, FAKE, FAKE, None, None) == 1
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        tv.argmax(torch.zeros(2, 8))

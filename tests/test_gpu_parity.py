@@ -1,0 +1,326 @@
+"""GPU parity: every libtv entry point against the CPU oracle on the same seeded inputs.
+
+Integer results (ancestor masks, depths, argmax, acceptance) must be bit exact. Attention
+must satisfy max-abs error <= 1e-2 and per-row relative L2 error <= 2e-2 (bf16 output,
+fp32 accumulation), and |lse error| <= 1e-3.
+"""
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import check_attention, dev_bf16, dev_i32, note
+from workloads import (accept_trial, chain_parent, kary_bfs_parent, make, random_tree_parent,
+                       rng_for, tie_rows)
+
+pytestmark = pytest.mark.gpu
+
+tv = pytest.importorskip("draft_tree_verification_tv_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tv.lib()
+
+
+# ------------------------------------------------------------------ a1 tree prep
+
+
+def tree_cases():
+    cases = [("chain1", chain_parent(1)), ("chain16", chain_parent(16)), ("chain256", chain_parent(256)),
+             ("kary256", kary_bfs_parent(256, 4)), ("kary85_3", kary_bfs_parent(85, 3))]
+    for n in (2, 5, 22, 63, 64, 65, 130, 256):
+        for seed in range(3):
+            cases.append((f"rand{n}_{seed}", random_tree_parent(rng_for(90, seed * 1000 + n), n, 16, 4)))
+    cases.append(("flat256", np.full(256, -1, dtype=np.int32)))
+    return cases
+
+
+def test_tree_prep_matches_oracle():
+    for name, parent in tree_cases():
+        anc, depth = tv.tree_prep(dev_i32(parent))
+        torch.cuda.synchronize()
+        exp_anc = oracle.anc_bitmask_words(parent)
+        exp_depth, _ = oracle.tree_structure(parent)
+        got = anc.cpu().numpy().view(np.uint64)
+        assert np.array_equal(got, exp_anc), name
+        assert np.array_equal(depth.cpu().numpy(), exp_depth), name
+
+
+def test_tree_prep_every_small_tree():
+    for n in range(1, 6):
+        for p in itertools.product(*[range(-1, i) for i in range(n)]):
+            parent = np.array(p, dtype=np.int32)
+            anc, depth = tv.tree_prep(dev_i32(parent))
+            assert np.array_equal(anc.cpu().numpy().view(np.uint64), oracle.anc_bitmask_words(parent))
+            assert np.array_equal(depth.cpu().numpy(), oracle.tree_structure(parent)[0])
+
+
+def test_bad_tree_reported_and_clamped():
+    bad = np.array([-1, 0, 5, 1, -7], dtype=np.int32)      # entries 2 and 4 are invalid
+    clamped = np.array([-1, 0, -1, 1, -1], dtype=np.int32)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    anc, depth = tv.tree_prep(dev_i32(bad), dev_error=err)
+    assert err.item() == 2
+    assert np.array_equal(anc.cpu().numpy().view(np.uint64), oracle.anc_bitmask_words(clamped))
+    err.zero_()
+    tv.tree_prep(dev_i32(clamped), dev_error=err)
+    assert err.item() == 0
+
+
+# ------------------------------------------------------------------ a6 accept
+
+
+def run_accept(parent, draft, tok):
+    ln, nodes, toks, bonus = tv.accept(dev_i32(parent), dev_i32(draft), dev_i32(tok))
+    return ln.item(), nodes.cpu().numpy(), toks.cpu().numpy(), bonus.item()
+
+
+def assert_accept_equal(parent, draft, tok, label):
+    ln, nodes, toks, bonus = run_accept(parent, draft, tok)
+    e_ln, e_nodes, e_toks, e_bonus = oracle.accept(parent, draft, tok)
+    n = len(parent)
+    assert ln == e_ln, label
+    assert nodes[:ln].tolist() == e_nodes.tolist(), label
+    assert toks[:ln].tolist() == e_toks.tolist(), label
+    assert (nodes[ln:] == -1).all() and (toks[ln:] == -1).all(), label
+    assert bonus == e_bonus, label
+    assert len(nodes) == n
+
+
+def test_accept_branch_8k_1000_trials():
+    for trial in range(1000):
+        parent, draft, tok, plen, pend = accept_trial("branch_8k", trial)
+        ln, nodes, _, _ = run_accept(parent, draft, tok)
+        assert ln == plen, trial
+        if plen:
+            assert nodes[ln - 1] == pend
+        if trial % 50 == 0:
+            assert_accept_equal(parent, draft, tok, f"branch_8k/{trial}")
+
+
+@pytest.mark.parametrize("name,trials", [("tiny_chain", 100), ("wide_tree", 50), ("max_256k", 30),
+                                         ("budget22", 100), ("decode_1node", 20)])
+def test_accept_planted(name, trials):
+    for trial in range(trials):
+        parent, draft, tok, _, _ = accept_trial(name, trial)
+        assert_accept_equal(parent, draft, tok, f"{name}/{trial}")
+
+
+def test_accept_random_small_vocab():
+    """Tiny vocabularies make many nodes match, so ties between paths are common."""
+    rng = np.random.default_rng(123)
+    for case in range(400):
+        n = int(rng.integers(1, 257)) if case % 4 == 0 else int(rng.integers(1, 20))
+        parent = np.array([-1] + [int(rng.integers(-1, i)) for i in range(1, n)], dtype=np.int32)
+        vocab = int(rng.integers(1, 4))
+        draft = rng.integers(0, vocab, n).astype(np.int32)
+        tok = rng.integers(0, vocab, n).astype(np.int32)
+        assert_accept_equal(parent, draft, tok, f"random/{case}")
+
+
+def test_accept_all_match_and_none():
+    w = make("wide_tree", 0, parts=("tree",), plant="all")
+    assert_accept_equal(w.parent, w.draft, w.draft, "wide all")
+    ln, nodes, _, _ = run_accept(w.parent, w.draft, w.draft)
+    assert ln == 4 and nodes[:4].tolist() == [0, 4, 20, 84]
+    assert_accept_equal(w.parent, w.draft, w.draft + 1, "wide none")
+
+
+# ------------------------------------------------------------------ a5 argmax
+
+
+def run_argmax(x, dtype, row_stride=None):
+    n, v = x.shape
+    if row_stride is not None and row_stride != v:
+        pad = np.zeros((n, row_stride), dtype=x.dtype)
+        pad[:, :v] = x
+        x_dev = pad
+    else:
+        x_dev = x
+    t = dev_bf16(x_dev) if dtype == "bf16" else torch.from_numpy(np.ascontiguousarray(x_dev)).cuda()
+    return tv.argmax(t, V=v).cpu().numpy()
+
+
+def oracle_rows(x, dtype):
+    return oracle.argmax_rows(oracle.bf16_bits_to_f64(x) if dtype == "bf16" else x.astype(np.float64))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", [1, 7, 8, 9, 100, 4095, 4096, 4097, 65536, 152063, 152064])
+def test_argmax_tie_rows(dtype, V):
+    rng = np.random.default_rng(V)
+    if V < 3:
+        x = rng.standard_normal((3, V)).astype(np.float32)
+        from workloads import bf16_bits_from_f32
+        x = bf16_bits_from_f32(x) if dtype == "bf16" else x
+    else:
+        x = tie_rows(rng, V, dtype)
+    exp = oracle_rows(x, dtype)
+    assert np.array_equal(run_argmax(x, dtype), exp)
+    assert np.array_equal(run_argmax(x, dtype, row_stride=V + 3), exp)     # unaligned rows
+
+
+@pytest.mark.parametrize("name,trials", [("tiny_chain", 10), ("branch_8k", 6), ("wide_tree", 2),
+                                         ("max_256k", 2), ("decode_1node", 3), ("budget22", 4)])
+def test_argmax_workloads(name, trials):
+    ties = 0
+    for trial in range(trials):
+        w = make(name, trial, parts=("tree", "logits"))
+        exp = oracle_rows(w.logits, w.logits_dtype)
+        got = run_argmax(w.logits, w.logits_dtype)
+        assert np.array_equal(got, exp), (name, trial)
+        x = oracle.bf16_bits_to_f64(w.logits) if w.logits_dtype == "bf16" else w.logits
+        ties += int(((x == x.max(axis=1, keepdims=True)).sum(axis=1) > 1).sum())
+    note(f"{name}: {ties} tied rows checked")
+
+
+def test_argmax_many_rows_reuses_workspace():
+    rng = np.random.default_rng(5)
+    ws = tv.argmax_workspace(300, 5000, "cuda")
+    for rep in range(3):
+        x = rng.standard_normal((300, 5000)).astype(np.float32)
+        x[:, 17] = x.max(axis=1) if rep == 1 else x[:, 17]
+        t = torch.from_numpy(x).cuda()
+        got = tv.argmax(t, workspace=ws).cpu().numpy()
+        assert np.array_equal(got, oracle.argmax_rows(x.astype(np.float64)))
+
+
+# ------------------------------------------------------------------ a2-a4 attention
+
+
+def attn_gpu(w, num_splits=0, with_lse=True):
+    q, k, v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+    lse = torch.empty((w.N, w.Hq), dtype=torch.float32, device="cuda") if with_lse else None
+    out = tv.tree_attn(q, k, v, dev_i32(w.parent), L=w.L, scale=w.scale, num_splits=num_splits, lse=lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def attn_ref(w):
+    return oracle.tree_attention(oracle.bf16_bits_to_f64(w.q), oracle.bf16_bits_to_f64(w.k),
+                                 oracle.bf16_bits_to_f64(w.v), w.parent, w.scale)
+
+
+@pytest.mark.parametrize("name,trials", [("tiny_chain", 4), ("budget22", 3)])
+def test_attention_small_workloads(name, trials):
+    for trial in range(trials):
+        w = make(name, trial)
+        note(f"attention {name} trial {trial}")
+        out, lse = attn_gpu(w)
+        ref, lref = attn_ref(w)
+        check_attention(out, ref, lse, lref, f"{name}/{trial}")
+
+
+EDGE = [
+    # (label, overrides)
+    ("L0_N1", dict(L=0, N=1, tree="chain", Hq=8, Hkv=2)),
+    ("L0_N22", dict(L=0, N=22, tree="random16", Hq=8, Hkv=8)),
+    ("L1_N5", dict(L=1, N=5, tree="random16", Hq=4, Hkv=1)),
+    ("L63_N1", dict(L=63, N=1, tree="chain", Hq=2, Hkv=2)),
+    ("L65_N3_mha", dict(L=65, N=3, tree="random16", Hq=1, Hkv=1)),
+    ("L1000_kary256_G1", dict(L=1000, N=256, tree="kary4", Hq=8, Hkv=8)),
+    ("L300_kary256_G8", dict(L=300, N=256, tree="kary4", Hq=16, Hkv=2)),
+    ("L777_G6_chain16", dict(L=777, N=16, tree="chain", Hq=24, Hkv=4)),
+    ("L4097_N64", dict(L=4097, N=64, tree="random16", Hq=32, Hkv=8)),
+    ("L2048_N40_G5", dict(L=2048, N=40, tree="random16", Hq=10, Hkv=2)),
+]
+
+
+@pytest.mark.parametrize("label,ov", EDGE, ids=[e[0] for e in EDGE])
+def test_attention_edge_shapes(label, ov):
+    w = make("budget22", 7, **ov)
+    note(f"attention edge {label}")
+    out, lse = attn_gpu(w)
+    ref, lref = attn_ref(w)
+    check_attention(out, ref, lse, lref, label)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 40, 1024])
+def test_attention_forced_splits(splits):
+    w = make("budget22", 11, L=2500, N=22)
+    note(f"attention forced splits {splits}")
+    out, lse = attn_gpu(w, num_splits=splits)
+    ref, lref = attn_ref(w)
+    check_attention(out, ref, lse, lref, f"splits={splits}")
+
+
+def test_attention_peaky_keys():
+    w = make("max_256k", 1, L=20000)
+    note("attention peaky 20k")
+    out, lse = attn_gpu(w)
+    ref, lref = attn_ref(w)
+    check_attention(out, ref, lse, lref, "peaky")
+
+
+def test_attention_strided_cache():
+    """K/V given as views into a larger cache ([T, 2*Hkv, D], using even heads)."""
+    w = make("budget22", 3, L=1500)
+    big_k = np.zeros((w.L + w.N + 5, 2 * w.Hkv, 128), dtype=np.uint16)
+    big_v = np.zeros_like(big_k)
+    big_k[: w.L + w.N, ::2] = w.k
+    big_v[: w.L + w.N, ::2] = w.v
+    kd, vd = dev_bf16(big_k)[:, ::2], dev_bf16(big_v)[:, ::2]
+    out = tv.tree_attn(dev_bf16(w.q), kd, vd, dev_i32(w.parent), L=w.L, scale=w.scale)
+    ref, _ = attn_ref(w)
+    check_attention(out, ref, label="strided")
+
+
+def test_attention_bad_tree_flag():
+    w = make("budget22", 2, L=200)
+    bad = w.parent.copy()
+    bad[5] = 9
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = tv.tree_attn(dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v), dev_i32(bad), L=w.L, scale=w.scale,
+                       dev_error=err)
+    torch.cuda.synchronize()
+    assert err.item() == 2
+    fixed = bad.copy()
+    fixed[5] = -1
+    ref, _ = oracle.tree_attention(oracle.bf16_bits_to_f64(w.q), oracle.bf16_bits_to_f64(w.k),
+                                   oracle.bf16_bits_to_f64(w.v), fixed, w.scale)
+    check_attention(out, ref, label="clamped tree")
+
+
+# ---------------------------------------------------------- full-size workloads
+
+
+@pytest.mark.parametrize("name,trial", [("branch_8k", 0), ("branch_8k", 1), ("long_128k", 0),
+                                        ("max_256k", 0), ("wide_tree", 0), ("decode_1node", 0)])
+def test_attention_full_size(name, trial):
+    note(f"full-size attention {name} trial {trial}: generating")
+    w = make(name, trial, parts=("tree", "qkv"))
+    note(f"full-size attention {name}: gpu")
+    out, lse = attn_gpu(w)
+    note(f"full-size attention {name}: oracle")
+    ref, lref = attn_ref(w)
+    e, r = check_attention(out, ref, lse, lref, f"{name}/{trial}")
+    note(f"{name}: max abs {e:.2e} row rel {r:.2e}")
+
+
+# ---------------------------------------------------------- whole verify step
+
+
+@pytest.mark.parametrize("name,trial", [("tiny_chain", 0), ("tiny_chain", 5), ("budget22", 1),
+                                        ("branch_8k", 2)])
+def test_verify_pipeline(name, trial):
+    w = make(name, trial)
+    logits = dev_bf16(w.logits) if w.logits_dtype == "bf16" else torch.from_numpy(w.logits).cuda()
+    out, tok, (ln, nodes, toks, bonus) = tv.verify(dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v),
+                                                   dev_i32(w.parent), logits, dev_i32(w.draft), L=w.L,
+                                                   scale=w.scale)
+    ref, _, etok, (eln, enodes, etoks, ebonus) = oracle.verify(
+        oracle.bf16_bits_to_f64(w.q), oracle.bf16_bits_to_f64(w.k), oracle.bf16_bits_to_f64(w.v), w.parent,
+        w.scale, oracle.bf16_bits_to_f64(w.logits) if w.logits_dtype == "bf16" else w.logits, w.draft)
+    check_attention(out, ref, label=name)
+    assert np.array_equal(tok.cpu().numpy(), etok)
+    assert ln.item() == eln == w.planted_len
+    assert nodes.cpu().numpy()[:eln].tolist() == enodes.tolist()
+    assert toks.cpu().numpy()[:eln].tolist() == etoks.tolist()
+    assert bonus.item() == ebonus
