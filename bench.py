@@ -156,12 +156,13 @@ def main():
         ref, _ = oracle.tree_attention(qf, kf, vf, w.parent, w.scale)
         got = out[:, sub].float().cpu().numpy().astype(np.float64)
         err = float(np.abs(got - ref).max())
+        excess = float((np.abs(got - ref) - (1e-2 + 2e-2 * np.abs(ref))).max())
         rel = float((np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)).max())
         etok = oracle.argmax_rows(oracle.bf16_bits_to_f64(w.logits))
         eln = oracle.accept(w.parent, w.draft, etok)[0]
         parity = {"attn_max_abs": err, "attn_row_rel": rel, "argmax_exact": bool((tok.cpu().numpy() == etok).all()),
                   "accept_exact": int(acc[0].item()) == eln, "accept_len": eln}
-        ok = err <= 1e-2 and rel <= 2e-2 and parity["argmax_exact"] and parity["accept_exact"]
+        ok = excess <= 0 and rel <= 2e-2 and parity["argmax_exact"] and parity["accept_exact"]
         log(f"parity {'OK' if ok else 'FAILED'}: {parity}")
         if not ok:
             sys.exit(1)

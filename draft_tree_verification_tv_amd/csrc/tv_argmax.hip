@@ -2,10 +2,10 @@
 // the temperature-0 sample, i.e. the argmax; DFlash contributor guide, discosf.com/news/
 // 4742660, "Coding conventions"). Lowest index on ties, bit exact.
 //
-// HBM-bound scan. Each workgroup owns one slice of one row and streams it with 16-byte
-// loads. Per thread, only the running maximum and the position of the first vector that
-// raised it are tracked (a max over the vector plus one compare); the element index is
-// recovered once at the end by re-reading that single vector. Partial (value, index)
+// HBM-bound scan. Each workgroup owns one slice of one row; every thread issues four
+// independent 16-byte loads before touching any of them, so each CU keeps 64 KB in
+// flight. Per vector only a max and one compare are spent; the element index is looked
+// up once, in the winning vector, which is still in registers. Partial (value, index)
 // pairs go to the workspace and the last workgroup of the row, found with a counter,
 // reduces them and restores the counter to zero.
 #include <climits>
@@ -17,7 +17,7 @@ namespace tv {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int kTargetWGs = 1024;
+constexpr int kUnroll = 4;
 
 struct Best {
   float v;
@@ -39,16 +39,14 @@ __device__ __forceinline__ Best wave_reduce(Best x) {
   return x;
 }
 
-template <bool kF32, bool kVec>
-__device__ __forceinline__ void load_vec(const char* row, int e, float (&x)[8]) {
+template <bool kF32>
+__device__ __forceinline__ void unpack(const u32x4 w, float (&x)[8]) {
   if constexpr (kF32) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(row + (int64_t)e * 4);
     x[0] = __uint_as_float(w[0]);
     x[1] = __uint_as_float(w[1]);
     x[2] = __uint_as_float(w[2]);
     x[3] = __uint_as_float(w[3]);
   } else {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(row + (int64_t)e * 2);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       x[2 * j] = bf16_lo(w[j]);
@@ -70,46 +68,77 @@ __global__ __launch_bounds__(kBlock) void argmax_kernel(const char* __restrict__
                                                         float* __restrict__ part_v,
                                                         int* __restrict__ part_i,
                                                         unsigned* __restrict__ counters) {
-  constexpr int EPV = kVec ? (kF32 ? 4 : 8) : 1;  // elements per load
+  constexpr int EPV = kVec ? (kF32 ? 4 : 8) : 1;  // elements per 16-byte load
   const int row = blockIdx.y;
   const int c = blockIdx.x;
   const char* rp = logits + (int64_t)row * row_bytes;
   const int begin = c * chunk_len;
   const int end = min(V, begin + chunk_len);
 
-  float bv = -INFINITY;
-  int bvec = INT_MAX;  // start of the first vector holding bv
-  int e = begin + threadIdx.x * EPV;
-  if (e < end) bvec = e;
+  Best b{-INFINITY, INT_MAX};
   if constexpr (kVec) {
-    // Full vectors, two in flight per iteration.
-    for (; e + EPV <= end; e += kBlock * EPV) {
-      float x[8];
-      load_vec<kF32, kVec>(rp, e, x);
-      float m = x[0];
+    // kUnroll independent 16-byte loads per thread, issued before any compare. Thread
+    // tid owns vectors begin + (u * kBlock + tid) * EPV, ascending in u.
+    u32x4 raw[kUnroll];
 #pragma unroll
-      for (int j = 1; j < EPV; ++j) m = fmaxf(m, x[j]);
-      if (m > bv) {
-        bv = m;
-        bvec = e;
+    for (int u = 0; u < kUnroll; ++u) {
+      const int e = begin + (u * kBlock + (int)threadIdx.x) * EPV;
+      raw[u] = u32x4{0u, 0u, 0u, 0u};
+      if (e + EPV <= end) raw[u] = *reinterpret_cast<const u32x4*>(rp + (int64_t)e * (kF32 ? 4 : 2));
+    }
+    int bu = -1;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int e = begin + (u * kBlock + (int)threadIdx.x) * EPV;
+      if (e + EPV <= end) {
+        float x[8];
+        unpack<kF32>(raw[u], x);
+        float m = x[0];
+#pragma unroll
+        for (int j = 1; j < EPV; ++j) m = fmaxf(m, x[j]);
+        if (bu < 0 || m > b.v) {
+          b.v = m;
+          bu = u;
+        }
       }
     }
-  }
-  // Ragged tail (or the whole slice when rows are not 16-byte aligned).
-  for (; e < end; e += kBlock * EPV) {
-    const int lim = min(EPV, end - e);
-    float m = load_one<kF32>(rp, e);
-    for (int j = 1; j < lim; ++j) m = fmaxf(m, load_one<kF32>(rp, e + j));
-    if (m > bv) {
-      bv = m;
-      bvec = e;
+    // Element index inside the winning vector (first element equal to the maximum).
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u == bu) {
+        float x[8];
+        unpack<kF32>(raw[u], x);
+        const int e = begin + (u * kBlock + (int)threadIdx.x) * EPV;
+#pragma unroll
+        for (int j = EPV - 1; j >= 0; --j)
+          if (x[j] == b.v) b.i = e + j;
+      }
     }
-  }
-  Best b{bv, INT_MAX};
-  if (bvec != INT_MAX) {
-    const int lim = min(EPV, end - bvec);
-    for (int j = lim - 1; j >= 0; --j)
-      if (load_one<kF32>(rp, bvec + j) == bv) b.i = bvec + j;
+    // A vector cut by the end of the row is read element by element (it is the
+    // thread's last and highest-indexed vector, so ascending order is kept).
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int e = begin + (u * kBlock + (int)threadIdx.x) * EPV;
+      if (e < end && e + EPV > end) {
+        for (int j = e; j < end; ++j) {
+          const float x = load_one<kF32>(rp, j);
+          if (b.i == INT_MAX || x > b.v) {
+            b.v = x;
+            b.i = j;
+          }
+        }
+      }
+    }
+    if (b.i == INT_MAX) b.v = -INFINITY;
+  } else {
+    for (int e = begin + (int)threadIdx.x; e < end; e += kBlock) {
+      const float x = load_one<kF32>(rp, e);
+      if (b.i == INT_MAX || x > b.v) {
+        b.v = x;
+        b.i = e;
+      }
+    }
+    if (b.i == INT_MAX) b.v = -INFINITY;
   }
 
   __shared__ float sv[kBlock / 64];
@@ -141,8 +170,8 @@ __global__ __launch_bounds__(kBlock) void argmax_kernel(const char* __restrict__
   __threadfence();
   Best r{-INFINITY, INT_MAX};
   for (int j = threadIdx.x; j < chunks; j += kBlock) {
-    const float v = __builtin_nontemporal_load(&part_v[(int64_t)row * chunks + j]);
-    const int ix = __builtin_nontemporal_load(&part_i[(int64_t)row * chunks + j]);
+    const float v = __hip_atomic_load(&part_v[(int64_t)row * chunks + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int ix = __hip_atomic_load(&part_i[(int64_t)row * chunks + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     r = better(r, Best{v, ix});
   }
   r = wave_reduce(r);
@@ -161,21 +190,18 @@ __global__ __launch_bounds__(kBlock) void argmax_kernel(const char* __restrict__
 
 }  // namespace
 
-ArgmaxPlan argmax_plan(int N, int V) {
+ArgmaxPlan argmax_plan(int N, int V, int dtype, bool vec) {
+  // One slice = kUnroll 16-byte loads per thread: 8192 bf16 or 4096 fp32 elements. The
+  // scalar path (rows not 16-byte aligned) uses 4096-element slices.
+  (void)N;
   ArgmaxPlan p;
-  int chunks = (kTargetWGs + N - 1) / N;
-  const int max_chunks = V / 4096 > 0 ? V / 4096 : 1;  // keep slices >= 4096 elements
-  if (chunks > max_chunks) chunks = max_chunks;
-  if (chunks < 1) chunks = 1;
-  int len = (V + chunks - 1) / chunks;
-  len = (len + 7) / 8 * 8;
-  p.chunks = (V + len - 1) / len;
-  p.chunk_len = len;
+  p.chunk_len = (vec && dtype == TV_BF16) ? kBlock * 8 * kUnroll : kBlock * 4 * kUnroll;
+  p.chunks = (V + p.chunk_len - 1) / p.chunk_len;
   return p;
 }
 
 size_t argmax_workspace_bytes(int N, int V) {
-  const ArgmaxPlan p = argmax_plan(N, V);
+  const ArgmaxPlan p = argmax_plan(N, V, TV_F32, false);  // the most slices of any path
   const size_t parts = (size_t)N * p.chunks;
   size_t bytes = parts * sizeof(float);
   bytes = (bytes + 255) / 256 * 256;
@@ -187,8 +213,11 @@ size_t argmax_workspace_bytes(int N, int V) {
 
 hipError_t launch_argmax(const void* logits, int dtype, int N, int V, int64_t row_stride, int32_t* tok,
                          void* workspace, hipStream_t stream) {
-  const ArgmaxPlan p = argmax_plan(N, V);
-  const size_t parts = (size_t)N * p.chunks;
+  const int esize = dtype == TV_F32 ? 4 : 2;
+  const int64_t row_bytes = row_stride * esize;
+  const bool vec = ((uintptr_t)logits % 16 == 0) && (row_bytes % 16 == 0);
+  const ArgmaxPlan p = argmax_plan(N, V, dtype, vec);
+  const size_t parts = (size_t)N * argmax_plan(N, V, TV_F32, false).chunks;
   char* ws = static_cast<char*>(workspace);
   float* part_v = reinterpret_cast<float*>(ws);
   size_t off = (parts * sizeof(float) + 255) / 256 * 256;
@@ -196,9 +225,6 @@ hipError_t launch_argmax(const void* logits, int dtype, int N, int V, int64_t ro
   off += (parts * sizeof(int) + 255) / 256 * 256;
   unsigned* counters = reinterpret_cast<unsigned*>(ws + off);
 
-  const int esize = dtype == TV_F32 ? 4 : 2;
-  const int64_t row_bytes = row_stride * esize;
-  const bool vec = ((uintptr_t)logits % 16 == 0) && (row_bytes % 16 == 0);
   const dim3 grid(p.chunks, N);
   const char* lg = static_cast<const char*>(logits);
   if (dtype == TV_F32) {

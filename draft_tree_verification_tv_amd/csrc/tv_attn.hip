@@ -8,27 +8,32 @@
 // Design (split-KV flash decoding, MFMA form):
 //   * Rows. For KV head h the G = Hq/Hkv query heads of all N nodes are stacked into
 //     M = G*N rows (row r -> node r/G, q head h*G + r%G), so one K/V tile read from HBM
-//     is used by every row that needs it. A workgroup owns up to 256 rows (32 per wave).
+//     is used by every row that needs it. A workgroup owns up to 256 rows, 32 per wave.
 //   * Splits. The key sequence [0, L+N) is cut into S ranges; each workgroup streams one
 //     range for one (KV head, row tile) and writes a normalised fp32 partial output and
-//     its log2-sum-exp. A second kernel merges the partials.
+//     its log2-sum-exp. attn_merge_kernel combines the partials.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: the
-//     accumulator layout puts one query row per lane (16 keys per lane per 32-key
-//     block), so the running max / sum of the online softmax are lane-local (plus one
-//     exchange with lane ^ 32) and P^T can feed the P.V product as the B operand
-//     straight from registers. O^T = V^T P^T accumulates in 64 fp32 registers per lane.
-//   * LDS. K is staged row-major (272-byte rows: 16 bytes of padding keep the 128-bit
-//     MFMA operand reads conflict free). V is staged transposed (one row per head-dim
-//     index, keys contiguous) with the keys of each 16-key group permuted so that the
-//     eight keys a lane needs for one MFMA are one 16-byte read. Two stages; the next
-//     tile's global loads are in flight while the current tile is multiplied.
-//   * Softmax. exp2 with the scale folded into one FMA; the reference maximum is only
-//     raised when a tile exceeds it by more than 2^8 (lazy rescaling), which keeps the
-//     per-tile rescale of the 64 output registers off the common path.
-//   * Tree keys (rows L..L+N-1) are masked with per-node ancestor bitmasks built in LDS
-//     by the workgroups whose range reaches them.
-//   * Workgroup order is remapped so that consecutive work items (the splits of one KV
-//     head) run on the same XCD and share its L2.
+//     accumulator layout gives every lane one query row (16 keys per 32-key block), so the
+//     online-softmax statistics are lane-local (plus one exchange with lane ^ 32), and
+//     P^T feeds the P.V product as the B operand straight from registers. O^T = V^T P^T
+//     accumulates in 64 fp32 registers per lane.
+//   * Memory pipeline. K and V tiles (64 keys x 128 dims, bf16) stream from HBM through
+//     registers into a ring of three LDS stages, two tiles ahead of the MFMAs. Both are
+//     stored row-major with a 16-byte-chunk XOR swizzle: K rows are read as 128-bit MFMA
+//     A operands; V is read with ds_read_b64_tr_b16, whose 4x16 in-register transpose
+//     hands each lane four consecutive keys of one head-dim column -- exactly the k-run
+//     the P.V MFMA needs -- so V needs no transposition pass.
+//   * Ping-pong. The waves form two groups that share SIMDs pairwise. Group A runs
+//     QK(t), softmax(t), PV(t); group B runs softmax(t-1), PV(t-1), QK(t). While one wave
+//     of a SIMD is in its VALU-heavy softmax, the other issues MFMAs.
+//   * Softmax. exp2 with the scale folded into one FMA. The reference maximum is raised
+//     only when a tile exceeds it by more than 2^8 (lazy rescaling), so the 64-register
+//     rescale of O is off the common path. Row sums are accumulated from the bf16-rounded
+//     probabilities with v_dot2_f32_bf16, so numerator and denominator use the same values.
+//   * Tree keys (rows L..L+N-1) are masked with per-node ancestor bitmasks built in LDS by
+//     the workgroups whose range reaches them.
+//   * Work items are remapped so that consecutive ones (the splits of one KV head) land
+//     on the same XCD.
 #include <cmath>
 
 #include "tv_internal.h"
@@ -38,19 +43,20 @@ namespace tv {
 namespace {
 
 constexpr int D = TV_HEAD_DIM;
-constexpr int KT = 64;                 // keys per LDS tile
-constexpr int TILE_ROWS = 256;         // stacked rows per workgroup (8 waves x 32)
-constexpr int KROW = D * 2 + 16;       // bytes per staged K row
-constexpr int VROW = KT * 2 + 16;      // bytes per staged V^T row
-constexpr int K_BYTES = KT * KROW;
-constexpr int V_BYTES = D * VROW;
-constexpr int STAGE = K_BYTES + V_BYTES;
+constexpr int KT = 64;                         // keys per tile
+constexpr int TILE_ROWS = 256;                 // stacked rows per workgroup (8 waves x 32)
+constexpr int ROWB = D * 2;                    // bytes per K or V row (256)
+constexpr int TILE_B = KT * ROWB;              // 16 KB per K (or V) tile
+constexpr int STAGE_B = 2 * TILE_B;            // K + V
+constexpr int NSTAGE = 3;
 constexpr int TREE_ANC_BYTES = kMaxNodes * kAncWords * 8;
 constexpr int TREE_BYTES = TREE_ANC_BYTES + 2 * kMaxNodes * 4;
-constexpr int SMEM_BYTES = 2 * STAGE + TREE_BYTES;
+constexpr int SMEM_BYTES = NSTAGE * STAGE_B + TREE_BYTES;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleTh = 8.0f;
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 struct SplitParams {
   const uint16_t* q;
@@ -71,24 +77,24 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Position of the first key of quad qd (keys 4qd..4qd+3 of a tile) in a staged V^T row.
-// Within each 16-key group the middle quads swap, so that a lane's eight keys for one
-// MFMA step (4g..4g+3 and 8+4g..8+4g+3) are contiguous.
-__device__ __forceinline__ int vt_pos(int qd) {
-  return (qd >> 2) * 16 + (qd & 1) * 8 + ((qd >> 1) & 1) * 4;
-}
+// 16-byte-chunk swizzles. K: chunk c of row r lives at chunk c ^ (r & 15), so the 16 rows
+// a 128-bit read phase touches hit 16 different chunks. V: chunk c of row r lives at
+// c ^ swz_v(r) with swz_v = {0, 6, 10, 12}[r & 3]; the transposed reads touch 4
+// consecutive rows x 4 chunks per half-wave, which this maps onto distinct chunks (and
+// onto distinct chunk pairs modulo 8).
+__device__ __forceinline__ int swz_k(int r) { return r & 15; }
+__device__ __forceinline__ int swz_v(int r) { return (0xCA60 >> ((r & 3) * 4)) & 15; }
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
   constexpr int NT = NW * 64;
-  constexpr int KCH = KT * (D / 8);            // 16-byte K chunks per tile
-  constexpr int KPT = (KCH + NT - 1) / NT;     // per thread
-  constexpr int VIT = (KT / 4) * (D / 8);      // (4-key quad, 8-dim chunk) items per tile
-  constexpr int VPT = (VIT + NT - 1) / NT;
+  constexpr int CH = KT * (ROWB / 16);   // 16-byte chunks per K (or V) tile
+  constexpr int CPT = CH / NT;           // per thread
+  static_assert(CH % NT == 0, "threads must divide the tile");
 
   extern __shared__ __align__(16) char smem[];
-  uint64_t* anc = reinterpret_cast<uint64_t*>(smem + 2 * STAGE);
-  int* par = reinterpret_cast<int*>(smem + 2 * STAGE + TREE_ANC_BYTES);
+  uint64_t* anc = reinterpret_cast<uint64_t*>(smem + NSTAGE * STAGE_B);
+  int* par = reinterpret_cast<int*>(smem + NSTAGE * STAGE_B + TREE_ANC_BYTES);
   int* jmp = par + kMaxNodes;
 
   // ---- work item
@@ -106,6 +112,9 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
   const int lane = tid & 63;
   const int ql = lane & 31;
   const int grp = lane >> 5;
+  const int i16 = lane & 15;
+  const int g16 = (lane >> 4) & 1;
+  const bool group_a = wave < NW / 2;
 
   const int r = rt * TILE_ROWS + wave * 32 + ql;
   const bool rvalid = r < p.M;
@@ -132,63 +141,48 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
   const uint16_t* kbase = p.k + (int64_t)h * p.sh;
   const uint16_t* vbase = p.v + (int64_t)h * p.sh;
 
-  u32x4 kreg[KPT];
-  u32x4 vreg[VPT][4];
-
-  auto gload = [&](int kt0) {
+  // ---- per-lane LDS offsets
+  int koff[8];  // K row ql, chunk 2*s8 + grp
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * NT;
-      const int key = kt0 + (c >> 4);
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (c < KCH && key < p.T)
-        x = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * p.st + (c & 15) * 8);
-      kreg[i] = x;
+  for (int s8 = 0; s8 < 8; ++s8) koff[s8] = ql * ROWB + (((2 * s8 + grp) ^ swz_k(ql)) << 4);
+  int voff[4];  // V rows 4*grp + i16/4 (+8), head-dim columns db*32 + g16*16 + 4*(i16%4)
+  {
+    const int row = 4 * grp + (i16 >> 2);
+    const int sw = swz_v(row);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int chunk = db * 4 + g16 * 2 + ((i16 & 3) >> 1);
+      voff[db] = row * ROWB + ((chunk ^ sw) << 4) + (i16 & 1) * 8;
     }
+  }
+
+  // ---- global -> register -> LDS staging (CPT K chunks and CPT V chunks per thread)
+  u32x4 st0[2 * CPT], st1[2 * CPT];
+
+  auto gload = [&](u32x4(&st)[2 * CPT], int kt0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int it = tid + i * NT;
-      const int dc = it & 15;
-      const int qd = it >> 4;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = kt0 + qd * 4 + j;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (it < VIT && key < p.T)
-          x = *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * p.st + dc * 8);
-        vreg[i][j] = x;
+    for (int i = 0; i < CPT; ++i) {
+      const int id = tid + i * NT;
+      const int key = kt0 + (id >> 4);
+      const int64_t off = (int64_t)key * p.st + (id & 15) * 8;
+      u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
+      if (key < p.T) {
+        xk = *reinterpret_cast<const u32x4*>(kbase + off);
+        xv = *reinterpret_cast<const u32x4*>(vbase + off);
       }
+      st[i] = xk;
+      st[CPT + i] = xv;
     }
   };
-
-  auto lds_store = [&](int buf) {
-    char* Ks = smem + buf * STAGE;
-    char* Vs = Ks + K_BYTES;
+  auto lds_write = [&](const u32x4(&st)[2 * CPT], int stage) __attribute__((always_inline)) {
+    char* Ks = smem + stage * STAGE_B;
+    char* Vs = Ks + TILE_B;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * NT;
-      if (c < KCH) *reinterpret_cast<u32x4*>(Ks + (c >> 4) * KROW + (c & 15) * 16) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int it = tid + i * NT;
-      if (it < VIT) {
-        const int dc = it & 15;
-        const int qd = it >> 4;
-        char* dst = Vs + (dc * 8) * VROW + vt_pos(qd) * 2;
-        // 4 keys x 8 dims -> 8 rows (one per dim) of 4 keys.
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t a0 = vreg[i][0][e], a1 = vreg[i][1][e], a2 = vreg[i][2][e], a3 = vreg[i][3][e];
-          uint2 lo, hi;
-          lo.x = (a0 & 0xFFFFu) | (a1 << 16);
-          lo.y = (a2 & 0xFFFFu) | (a3 << 16);
-          hi.x = (a0 >> 16) | (a1 & 0xFFFF0000u);
-          hi.y = (a2 >> 16) | (a3 & 0xFFFF0000u);
-          *reinterpret_cast<uint2*>(dst + (2 * e) * VROW) = lo;
-          *reinterpret_cast<uint2*>(dst + (2 * e + 1) * VROW) = hi;
-        }
-      }
+    for (int i = 0; i < CPT; ++i) {
+      const int id = tid + i * NT;
+      const int row = id >> 4, c = id & 15;
+      *reinterpret_cast<u32x4*>(Ks + row * ROWB + ((c ^ swz_k(row)) << 4)) = st[i];
+      *reinterpret_cast<u32x4*>(Vs + row * ROWB + ((c ^ swz_v(row)) << 4)) = st[CPT + i];
     }
   };
 
@@ -197,32 +191,25 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
   float m_ref = -INFINITY;
   float lsum = 0.f;
+  f32x16 sc[2];
+  bf16x8 pb[4];
 
-  if (ntiles > 0) {
-    gload(kbeg);
-    lds_store(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int kt0 = kbeg + t * KT;
-    if (t + 1 < ntiles) gload(kt0 + KT);
-
-    const char* Ks = smem + (t & 1) * STAGE;
-    const char* Vs = Ks + K_BYTES;
-
-    // S^T for two 32-key blocks
-    f32x16 sc[2] = {f32x16{}, f32x16{}};
+  auto qk = [&](int stage) __attribute__((always_inline)) {
+    const char* Ks = smem + stage * STAGE_B;
+    sc[0] = f32x16{};
+    sc[1] = f32x16{};
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + ql) * KROW + s8 * 32 + grp * 16);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + kb * 32 * ROWB + koff[s8]);
         sc[kb] = mfma32(a, qf[s8], sc[kb]);
       }
     }
+  };
 
-    // Mask keys past the context: tree keys by ancestry, anything past L+N always.
+  // Keys past the context: tree keys by ancestry, anything past L+N never.
+  auto mask = [&](int kt0) __attribute__((always_inline)) {
     if (kt0 + KT > p.L) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -238,8 +225,10 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
         }
       }
     }
+  };
 
-    // Online softmax (log2 domain), lazily rescaled.
+  // Online softmax (log2 domain), lazily rescaled; leaves bf16 P^T fragments in pb.
+  auto softmax = [&]() __attribute__((always_inline)) {
     float mt = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) mt = fmaxf(mt, fmaxf(sc[0][e], sc[1][e]));
@@ -255,40 +244,75 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
       m_ref = m_new;
     }
     const float mu = m_ref == -INFINITY ? 0.f : m_ref;
-
-    bf16x8 pb[4];
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int th = 0; th < 2; ++th) {
-        f32x2 pr[4];
+        bf16x2 b[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][th * 8 + 2 * j], p.c, -mu));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][th * 8 + 2 * j + 1], p.c, -mu));
-          lsum += p0 + p1;
-          pr[j] = f32x2{p0, p1};
+          b[j] = __builtin_convertvector((f32x2{p0, p1}), bf16x2);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(b[j], ones, lsum, false);
         }
-        const bf16x2 b0 = __builtin_convertvector(pr[0], bf16x2);
-        const bf16x2 b1 = __builtin_convertvector(pr[1], bf16x2);
-        const bf16x2 b2 = __builtin_convertvector(pr[2], bf16x2);
-        const bf16x2 b3 = __builtin_convertvector(pr[3], bf16x2);
-        pb[kb * 2 + th] = bf16x8{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+        pb[kb * 2 + th] = bf16x8{b[0][0], b[0][1], b[1][0], b[1][1], b[2][0], b[2][1], b[3][0], b[3][1]};
       }
     }
+  };
 
-    // O^T += V^T P^T
+  // O^T += V^T P^T; V^T fragments come from the row-major V tile via transposed reads.
+  auto pv = [&](int stage) __attribute__((always_inline)) {
+    const char* Vs = smem + stage * STAGE_B + TILE_B;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vs + (db * 32 + ql) * VROW + ks * 32 + grp * 16);
-        o[db] = mfma32(a, pb[ks], o[db]);
+        const char* a0 = Vs + ks * 16 * ROWB + voff[db];
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * ROWB));
+        const i16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = mfma32(__builtin_bit_cast(bf16x8, a), pb[ks], o[db]);
       }
     }
+  };
 
-    if (t + 1 < ntiles) lds_store((t + 1) & 1);
+  // One pipeline step for tile t: loads for tile t+2 go into `ld`, tile t+1 is written
+  // to LDS from `wr`.
+  auto body = [&](int t, u32x4(&ld)[2 * CPT], const u32x4(&wr)[2 * CPT]) __attribute__((always_inline)) {
+    const int kt0 = kbeg + t * KT;
+    const int stage = t % NSTAGE;
+    if (t + 2 < ntiles) gload(ld, kt0 + 2 * KT);
+    if (group_a) {
+      qk(stage);
+      mask(kt0);
+      softmax();
+      if (t + 1 < ntiles) lds_write(wr, (t + 1) % NSTAGE);
+      pv(stage);
+    } else {
+      if (t > 0) {
+        softmax();
+        pv((t - 1) % NSTAGE);
+      }
+      if (t + 1 < ntiles) lds_write(wr, (t + 1) % NSTAGE);
+      qk(stage);
+      mask(kt0);
+    }
     __syncthreads();
+  };
+
+  if (ntiles > 0) gload(st0, kbeg);
+  if (ntiles > 1) gload(st1, kbeg + KT);
+  if (ntiles > 0) lds_write(st0, 0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    body(t, st0, st1);
+    if (t + 1 < ntiles) body(t + 1, st1, st0);
+  }
+  if (!group_a && ntiles > 0) {
+    softmax();
+    pv((ntiles - 1) % NSTAGE);
   }
 
   // ---- partial result of this split
@@ -319,10 +343,12 @@ struct MergeParams {
   int N, Hq, G, RT, S;
 };
 
-// One (node, q head) row per 32 threads; each thread merges 4 head-dim values:
+// One wave per (node, q head) row, two head-dim values per lane:
 // lse = M + log2 sum_s 2^(lse_s - M), out = sum_s 2^(lse_s - lse) * out_s.
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams mp) {
-  const int row = blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + wave;
   if (row >= mp.N * mp.Hq) return;
   const int n = row / mp.Hq;
   const int qh = row % mp.Hq;
@@ -330,29 +356,42 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams mp) {
   const int r = n * mp.G + qh % mp.G;
   const int rt = r / TILE_ROWS;
   const int64_t base0 = (int64_t)(h * mp.RT + rt) * mp.S * TILE_ROWS + (r % TILE_ROWS);
+  const float* lse_p = mp.part_lse + base0;
+  const float* o_p = mp.part_o + base0 * D + 2 * lane;
+
   float mx = -INFINITY;
-  for (int s = 0; s < mp.S; ++s) mx = fmaxf(mx, mp.part_lse[base0 + (int64_t)s * TILE_ROWS]);
-  const int d0 = (threadIdx.x & 31) * 4;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = lane; s < mp.S; s += 64) mx = fmaxf(mx, lse_p[(int64_t)s * TILE_ROWS]);
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+
+  f32x2 acc = {0.f, 0.f};
   float wsum = 0.f;
   if (mx != -INFINITY) {
-    for (int s = 0; s < mp.S; ++s) {
-      const int64_t b = base0 + (int64_t)s * TILE_ROWS;
-      const float wgt = exp2f(mp.part_lse[b] - mx);
+    int s = 0;
+    for (; s + 8 <= mp.S; s += 8) {
+      float l8[8];
+      f32x2 x8[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        l8[u] = lse_p[(int64_t)(s + u) * TILE_ROWS];
+        x8[u] = *reinterpret_cast<const f32x2*>(o_p + (int64_t)(s + u) * TILE_ROWS * D);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wgt = exp2f(l8[u] - mx);
+        wsum += wgt;
+        acc += wgt * x8[u];
+      }
+    }
+    for (; s < mp.S; ++s) {
+      const float wgt = exp2f(lse_p[(int64_t)s * TILE_ROWS] - mx);
       wsum += wgt;
-      const f32x4 x = *reinterpret_cast<const f32x4*>(mp.part_o + b * D + d0);
-      acc += wgt * x;
+      acc += wgt * *reinterpret_cast<const f32x2*>(o_p + (int64_t)s * TILE_ROWS * D);
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  const bf16x2 lo = __builtin_convertvector((f32x2{acc[0] * inv, acc[1] * inv}), bf16x2);
-  const bf16x2 hi = __builtin_convertvector((f32x2{acc[2] * inv, acc[3] * inv}), bf16x2);
-  uint2 packed;
-  packed.x = __builtin_bit_cast(uint32_t, lo);
-  packed.y = __builtin_bit_cast(uint32_t, hi);
-  *reinterpret_cast<uint2*>(mp.out + (int64_t)row * D + d0) = packed;
-  if (mp.lse && (threadIdx.x & 31) == 0)
-    mp.lse[row] = mx == -INFINITY ? -INFINITY : (mx + __log2f(wsum)) * kLn2;
+  const bf16x2 ob = __builtin_convertvector((f32x2{acc[0] * inv, acc[1] * inv}), bf16x2);
+  *reinterpret_cast<bf16x2*>(mp.out + (int64_t)row * D + 2 * lane) = ob;
+  if (mp.lse && lane == 0) mp.lse[row] = mx == -INFINITY ? -INFINITY : (mx + __log2f(wsum)) * kLn2;
 }
 
 template <int NW>
@@ -376,17 +415,15 @@ AttnPlan attn_plan(int N, int L, int Hq, int Hkv, int num_splits, int num_cus) {
   p.M = p.G * N;
   p.RT = (p.M + TILE_ROWS - 1) / TILE_ROWS;
   const int rows = p.M < TILE_ROWS ? p.M : TILE_ROWS;
-  p.NW = (rows + 31) / 32;
-  if (p.NW < 2) p.NW = 2;
+  p.NW = rows <= 64 ? 2 : rows <= 128 ? 4 : 8;
   p.T = L + N;
   const int tiles = (p.T + KT - 1) / KT;
   int S = num_splits;
   if (S <= 0) {
-    // One workgroup per CU for 8-wave groups (register bound), two for smaller groups
-    // (LDS bound); at least 8 tiles per split so partial traffic stays small.
-    const int per_cu = p.NW > 4 ? 1 : 2;
+    // One workgroup per CU (the three LDS stages take 106 KB); at least 8 tiles per split
+    // so that partial-output traffic stays small against the KV stream.
     const int units = Hkv * p.RT;
-    S = (num_cus * per_cu + units - 1) / units;
+    S = (num_cus + units - 1) / units;
     const int cap = tiles / 8 > 0 ? tiles / 8 : 1;
     if (S > cap) S = cap;
   }
@@ -440,11 +477,7 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const void* q, const void* k, 
   hipError_t e;
   switch (plan.NW) {
     case 2: e = launch_split<2>(sp, nwg, stream); break;
-    case 3: e = launch_split<3>(sp, nwg, stream); break;
     case 4: e = launch_split<4>(sp, nwg, stream); break;
-    case 5: e = launch_split<5>(sp, nwg, stream); break;
-    case 6: e = launch_split<6>(sp, nwg, stream); break;
-    case 7: e = launch_split<7>(sp, nwg, stream); break;
     default: e = launch_split<8>(sp, nwg, stream); break;
   }
   if (e != hipSuccess) return e;
@@ -460,7 +493,7 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const void* q, const void* k, 
   mp.RT = plan.RT;
   mp.S = plan.S;
   const int rows_out = N * Hq;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3((rows_out + 7) / 8), dim3(256), 0, stream, mp);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((rows_out + 3) / 4), dim3(256), 0, stream, mp);
   return hipGetLastError();
 }
 

@@ -14,6 +14,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kMaxNodes = TV_MAX_NODES;
 constexpr int kAncWords = 4;
@@ -87,7 +89,7 @@ struct ArgmaxPlan {
   int chunks;     // workgroups per row
   int chunk_len;  // elements per workgroup (multiple of 8)
 };
-ArgmaxPlan argmax_plan(int N, int V);
+ArgmaxPlan argmax_plan(int N, int V, int dtype, bool vec);
 size_t argmax_workspace_bytes(int N, int V);
 hipError_t launch_argmax(const void* logits, int dtype, int N, int V, int64_t row_stride,
                          int32_t* tok, void* workspace, hipStream_t stream);
@@ -95,7 +97,7 @@ hipError_t launch_argmax(const void* logits, int dtype, int N, int V, int64_t ro
 struct AttnPlan {
   int G, M;        // q heads per KV head; stacked rows per KV head (G * N)
   int RT;          // row tiles of up to 256 stacked rows
-  int NW;          // waves per workgroup (rows per tile / 32, at least 2)
+  int NW;          // waves per workgroup: 2, 4 or 8 (32 rows each)
   int S;           // KV splits actually launched
   int KS;          // keys per split (multiple of the key tile)
   int T;           // L + N

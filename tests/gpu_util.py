@@ -5,7 +5,12 @@ import sys
 import numpy as np
 import torch
 
-ATOL = 1e-2        # max |out - ref| over the tensor
+# Elementwise |out - ref| <= ATOL + RTOL * |ref| (the allclose reading of "max-abs 1e-2 and
+# relative 2e-2"): a bf16 output alone is off by up to half an ulp, 2^-9 |ref|, which
+# exceeds 1e-2 once |ref| >= 4 (peaky rows reach that). RTOL_ROW guards the other side: a
+# per-row relative L2 bound, so an all-zero output cannot pass on rows with small norms.
+ATOL = 1e-2
+RTOL = 2e-2
 RTOL_ROW = 2e-2    # per (node, head) row: ||out - ref|| / ||ref||
 LSE_ATOL = 1e-3
 
@@ -29,12 +34,14 @@ def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
 
 def check_attention(out: torch.Tensor, ref: np.ndarray, lse: torch.Tensor = None,
                     lse_ref: np.ndarray = None, label: str = ""):
-    """Both bounds must hold: max-abs over the tensor and the per-row relative L2 error."""
+    """Both bounds must hold: elementwise atol/rtol and the per-row relative L2 error."""
     o = bf16_to_f64(out)
     assert np.isfinite(o).all(), f"{label}: non-finite output"
     err = np.abs(o - ref)
     rel = np.linalg.norm(o - ref, axis=-1) / np.maximum(np.linalg.norm(ref, axis=-1), 1e-30)
-    assert err.max() <= ATOL, f"{label}: max abs err {err.max():.3e}"
+    excess = err - (ATOL + RTOL * np.abs(ref))
+    assert excess.max() <= 0, (f"{label}: elementwise bound exceeded by {excess.max():.3e} "
+                               f"(max abs err {err.max():.3e})")
     assert rel.max() <= RTOL_ROW, f"{label}: max row rel err {rel.max():.3e}"
     if lse is not None:
         le = np.abs(lse.cpu().numpy().astype(np.float64) - lse_ref)
