@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-check", action="store_true", help="skip the parity re-check")
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--splits", type=int, default=0, help="force the KV split count (0 = library choice)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -108,6 +110,16 @@ def main():
         tv.accept(parent, draft, tok, out=acc, stream=stream)
         if ev:
             ev[3].record(stream)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.copy_probe_mib} MiB read + written once")
+        del src, dst
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):

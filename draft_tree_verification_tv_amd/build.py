@@ -20,11 +20,15 @@ LIB_DIR = os.path.join(PKG_DIR, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libtv.so")
 SOURCES = ["tv_api.hip", "tv_attn.hip", "tv_argmax.hip", "tv_tree.hip"]
 ARCH = "gfx950"
+# Per-file extras. Attention never produces or consumes NaN on valid input (masking uses
+# -inf, which stays honoured), so fmaxf needs no NaN canonicalisation there; the argmax
+# keeps IEEE NaN semantics.
+EXTRA = {"tv_attn.hip": ["-fno-honor-nans"]}
 
 # Packed fp32 VALU ops are disabled for all device code: the kernels rely on plain
 # scalar fp32 arithmetic only.
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
@@ -37,24 +41,43 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; a ROCm toolchain is required to build libtv")
 
 
+def _run(cmd, verbose):
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(ln for ln in res.stderr.splitlines() if noise not in ln)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libtv.so (always recompiles). Returns its path."""
+    """Compile every HIP source and link libtv.so (always recompiles). Returns its path."""
     os.makedirs(LIB_DIR, exist_ok=True)
-    fd, tmp = tempfile.mkstemp(prefix="libtv.", suffix=".so.tmp", dir=LIB_DIR)
-    os.close(fd)
-    cmd = [hipcc(), *FLAGS, f"-I{INCLUDE}", *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    try:
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        noise = "is not a recognized feature for this target"
-        err = "\n".join(ln for ln in res.stderr.splitlines() if noise not in ln)
-        if res.returncode != 0:
-            raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{err}")
-        if verbose and err.strip():
-            print(err, file=sys.stderr)
-        os.replace(tmp, LIB_PATH)
-    finally:
-        if os.path.exists(tmp):
-            os.unlink(tmp)
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="tvbuild.") as tmpdir:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, src + ".o")
+            cmd = [cc, *FLAGS, *EXTRA.get(src, []), f"-I{INCLUDE}", "-c", os.path.join(CSRC, src), "-o", obj]
+            procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+            objs.append(obj)
+        for cmd, pr in procs:
+            _, err = pr.communicate()
+            noise = "is not a recognized feature for this target"
+            err = "\n".join(ln for ln in err.splitlines() if noise not in ln)
+            if pr.returncode != 0:
+                raise RuntimeError(f"hipcc failed ({pr.returncode}):\n{' '.join(cmd)}\n{err}")
+            if verbose and err.strip():
+                print(err, file=sys.stderr)
+        fd, tmp = tempfile.mkstemp(prefix="libtv.", suffix=".so.tmp", dir=LIB_DIR)
+        os.close(fd)
+        try:
+            _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+            os.replace(tmp, LIB_PATH)
+        finally:
+            if os.path.exists(tmp):
+                os.unlink(tmp)
     return LIB_PATH
 
 

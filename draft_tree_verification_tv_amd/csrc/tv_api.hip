@@ -83,6 +83,8 @@ int tv_tree_attn(const void* q, const void* k, const void* v, int64_t kv_stride_
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return TV_ERR_INVALID_ARG;
   if (kv_stride_t < 0 || kv_stride_h < 0 || kv_stride_t % 8 || kv_stride_h % 8) return TV_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return TV_ERR_INVALID_ARG;
+  // One KV head's rows must be addressable with 32-bit byte offsets.
+  if (((int64_t)L + N) * kv_stride_t * 2 + 4096 > (int64_t)UINT32_MAX) return TV_ERR_UNSUPPORTED;
   const tv::AttnPlan p = tv::attn_plan(N, L, Hq, Hkv, num_splits, cu_count());
   const size_t need = tv::attn_workspace_bytes(p, Hkv);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return TV_ERR_WORKSPACE;

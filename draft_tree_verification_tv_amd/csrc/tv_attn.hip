@@ -17,19 +17,22 @@
 //     online-softmax statistics are lane-local (plus one exchange with lane ^ 32), and
 //     P^T feeds the P.V product as the B operand straight from registers. O^T = V^T P^T
 //     accumulates in 64 fp32 registers per lane.
-//   * Memory pipeline. K and V tiles (64 keys x 128 dims, bf16) stream from HBM through
-//     registers into a ring of three LDS stages, two tiles ahead of the MFMAs. Both are
-//     stored row-major with a 16-byte-chunk XOR swizzle: K rows are read as 128-bit MFMA
-//     A operands; V is read with ds_read_b64_tr_b16, whose 4x16 in-register transpose
-//     hands each lane four consecutive keys of one head-dim column -- exactly the k-run
-//     the P.V MFMA needs -- so V needs no transposition pass.
+//   * Memory pipeline. K and V tiles (64 keys x 128 dims, bf16) are copied HBM -> LDS by
+//     global_load_lds_dwordx4 (no registers involved) into a ring of four stages, two
+//     tiles ahead of the MFMAs; each wave waits only for the tile it needs next and the
+//     barrier drains LDS traffic only, so 64 KB per CU stay in flight. Both tiles are
+//     row-major with a 16-byte-chunk XOR swizzle: K rows are read as 128-bit MFMA A
+//     operands; V is read with ds_read_b64_tr_b16, whose 4x16 in-register transpose hands
+//     each lane four consecutive keys of one head-dim column -- exactly the k-run the P.V
+//     MFMA needs -- so V needs no transposition pass.
 //   * Ping-pong. The waves form two groups that share SIMDs pairwise. Group A runs
 //     QK(t), softmax(t), PV(t); group B runs softmax(t-1), PV(t-1), QK(t). While one wave
 //     of a SIMD is in its VALU-heavy softmax, the other issues MFMAs.
 //   * Softmax. exp2 with the scale folded into one FMA. The reference maximum is raised
 //     only when a tile exceeds it by more than 2^8 (lazy rescaling), so the 64-register
-//     rescale of O is off the common path. Row sums are accumulated from the bf16-rounded
-//     probabilities with v_dot2_f32_bf16, so numerator and denominator use the same values.
+//     rescale of O is off the common path. Row sums use the unrounded fp32 probabilities
+//     (so the exported log-sum-exp is exact to fp32); P is rounded to bf16 only as the
+//     MFMA operand.
 //   * Tree keys (rows L..L+N-1) are masked with per-node ancestor bitmasks built in LDS by
 //     the workgroups whose range reaches them.
 //   * Work items are remapped so that consecutive ones (the splits of one KV head) land
@@ -48,7 +51,7 @@ constexpr int TILE_ROWS = 256;                 // stacked rows per workgroup (8 
 constexpr int ROWB = D * 2;                    // bytes per K or V row (256)
 constexpr int TILE_B = KT * ROWB;              // 16 KB per K (or V) tile
 constexpr int STAGE_B = 2 * TILE_B;            // K + V
-constexpr int NSTAGE = 3;
+constexpr int NSTAGE = 4;                      // LDS ring: tiles t-1 .. t+2
 constexpr int TREE_ANC_BYTES = kMaxNodes * kAncWords * 8;
 constexpr int TREE_BYTES = TREE_ANC_BYTES + 2 * kMaxNodes * 4;
 constexpr int SMEM_BYTES = NSTAGE * STAGE_B + TREE_BYTES;
@@ -85,12 +88,36 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ int swz_k(int r) { return r & 15; }
 __device__ __forceinline__ int swz_v(int r) { return (0xCA60 >> ((r & 3) * 4)) & 15; }
 
+// Asynchronous 16-byte-per-lane copy from global memory straight into LDS
+// (global_load_lds_dwordx4): lane i's 16 bytes at gbase + goff land at LDS byte
+// lds + 16*i. No VGPR receives data, so nothing can be overwritten while the copy is in
+// flight; completion is tracked by vmcnt. M0 carries the LDS address and is restored.
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t goff, const void* gbase) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(goff), "s"(gbase)
+      : "memory");
+}
+
+// Workgroup barrier that waits for this wave's LDS traffic and for all but its newest
+// kPending vector-memory operations (the copies of the tile after next stay in flight).
+// No release fence: outstanding global loads are deliberately not drained.
+template <int kPending>
+__device__ __forceinline__ void barrier_keep(void) {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(kPending) : "memory");
+}
+
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
-  constexpr int NT = NW * 64;
-  constexpr int CH = KT * (ROWB / 16);   // 16-byte chunks per K (or V) tile
-  constexpr int CPT = CH / NT;           // per thread
-  static_assert(CH % NT == 0, "threads must divide the tile");
+  constexpr int BLK = KT / 4;            // 1 KB blocks per K (or V) tile
+  constexpr int BPW = BLK / NW;          // blocks of each per wave
+  constexpr int DPT = 2 * BPW;           // copies per wave per tile
+  static_assert(BLK % NW == 0, "waves must divide the tile");
 
   extern __shared__ __align__(16) char smem[];
   uint64_t* anc = reinterpret_cast<uint64_t*>(smem + NSTAGE * STAGE_B);
@@ -108,7 +135,7 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
   const int h = w / (p.RT * p.S);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int lane = tid & 63;
   const int ql = lane & 31;
   const int grp = lane >> 5;
@@ -156,33 +183,45 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
     }
   }
 
-  // ---- global -> register -> LDS staging (CPT K chunks and CPT V chunks per thread)
-  u32x4 st0[2 * CPT], st1[2 * CPT];
+  // ---- HBM -> LDS copies. A tile's K (and V) is 16 blocks of 4 rows x 256 bytes; wave w
+  // copies blocks w, w + NW, ... of both. Lane i of a block copy fills LDS row
+  // 4b + i/16, physical chunk i%16, so it loads logical chunk (i%16) ^ swizzle(row).
+  // Offsets within one KV head are 32-bit (the host guarantees (L+N) rows fit).
+  const char* kb8 = reinterpret_cast<const char*>(kbase);
+  const char* vb8 = reinterpret_cast<const char*>(vbase);
+  const uint32_t rowstride_b = (uint32_t)p.st * 2u;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
+  uint32_t dk[BPW], dv[BPW];
+#pragma unroll
+  for (int j = 0; j < BPW; ++j) {
+    const int row = 4 * (wave + j * NW) + (lane >> 4);
+    const int pc = lane & 15;
+    dk[j] = (uint32_t)row * rowstride_b + (uint32_t)((pc ^ swz_k(row)) << 4);
+    dv[j] = (uint32_t)row * rowstride_b + (uint32_t)((pc ^ swz_v(row)) << 4);
+  }
 
-  auto gload = [&](u32x4(&st)[2 * CPT], int kt0) __attribute__((always_inline)) {
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const int kt0 = kbeg + t * KT;
+    const uint32_t st_lds = lds_base + (uint32_t)((t & (NSTAGE - 1)) * STAGE_B);
+    if (kt0 + KT <= p.T) {
+      const uint32_t base = (uint32_t)kt0 * rowstride_b;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int id = tid + i * NT;
-      const int key = kt0 + (id >> 4);
-      const int64_t off = (int64_t)key * p.st + (id & 15) * 8;
-      u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
-      if (key < p.T) {
-        xk = *reinterpret_cast<const u32x4*>(kbase + off);
-        xv = *reinterpret_cast<const u32x4*>(vbase + off);
+      for (int j = 0; j < BPW; ++j) {
+        const uint32_t blk = (uint32_t)((wave + j * NW) * 1024);
+        dma16(st_lds + blk, base + dk[j], kb8);
+        dma16(st_lds + TILE_B + blk, base + dv[j], vb8);
       }
-      st[i] = xk;
-      st[CPT + i] = xv;
-    }
-  };
-  auto lds_write = [&](const u32x4(&st)[2 * CPT], int stage) __attribute__((always_inline)) {
-    char* Ks = smem + stage * STAGE_B;
-    char* Vs = Ks + TILE_B;
+    } else {
+      // Last tile of the sequence: rows past L+N re-read row L+N-1 (always masked).
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int id = tid + i * NT;
-      const int row = id >> 4, c = id & 15;
-      *reinterpret_cast<u32x4*>(Ks + row * ROWB + ((c ^ swz_k(row)) << 4)) = st[i];
-      *reinterpret_cast<u32x4*>(Vs + row * ROWB + ((c ^ swz_v(row)) << 4)) = st[CPT + i];
+      for (int j = 0; j < BPW; ++j) {
+        const int row = 4 * (wave + j * NW) + (lane >> 4);
+        const int pc = lane & 15;
+        const uint32_t grow = (uint32_t)min(kt0 + row, p.T - 1) * rowstride_b;
+        const uint32_t blk = (uint32_t)((wave + j * NW) * 1024);
+        dma16(st_lds + blk, grow + (uint32_t)((pc ^ swz_k(row)) << 4), kb8);
+        dma16(st_lds + TILE_B + blk, grow + (uint32_t)((pc ^ swz_v(row)) << 4), vb8);
+      }
     }
   };
 
@@ -244,7 +283,6 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
       m_ref = m_new;
     }
     const float mu = m_ref == -INFINITY ? 0.f : m_ref;
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -255,7 +293,7 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][th * 8 + 2 * j], p.c, -mu));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][th * 8 + 2 * j + 1], p.c, -mu));
           b[j] = __builtin_convertvector((f32x2{p0, p1}), bf16x2);
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(b[j], ones, lsum, false);
+          lsum += p0 + p1;
         }
         pb[kb * 2 + th] = bf16x8{b[0][0], b[0][1], b[1][0], b[1][1], b[2][0], b[2][1], b[3][0], b[3][1]};
       }
@@ -278,41 +316,43 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
     }
   };
 
-  // One pipeline step for tile t: loads for tile t+2 go into `ld`, tile t+1 is written
-  // to LDS from `wr`.
-  auto body = [&](int t, u32x4(&ld)[2 * CPT], const u32x4(&wr)[2 * CPT]) __attribute__((always_inline)) {
+  // One pipeline step for tile t: tile t+2 starts streaming into LDS; tile t+1 must have
+  // landed before the closing barrier.
+  auto body = [&](int t) __attribute__((always_inline)) {
     const int kt0 = kbeg + t * KT;
-    const int stage = t % NSTAGE;
-    if (t + 2 < ntiles) gload(ld, kt0 + 2 * KT);
+    const int stage = t & (NSTAGE - 1);
+    if (t + 2 < ntiles) issue(t + 2);
     if (group_a) {
       qk(stage);
       mask(kt0);
       softmax();
-      if (t + 1 < ntiles) lds_write(wr, (t + 1) % NSTAGE);
       pv(stage);
     } else {
       if (t > 0) {
         softmax();
-        pv((t - 1) % NSTAGE);
+        pv((t - 1) & (NSTAGE - 1));
       }
-      if (t + 1 < ntiles) lds_write(wr, (t + 1) % NSTAGE);
       qk(stage);
       mask(kt0);
     }
-    __syncthreads();
+    if (t + 2 < ntiles)
+      barrier_keep<DPT>();
+    else
+      barrier_keep<0>();
   };
 
-  if (ntiles > 0) gload(st0, kbeg);
-  if (ntiles > 1) gload(st1, kbeg + KT);
-  if (ntiles > 0) lds_write(st0, 0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
-    body(t, st0, st1);
-    if (t + 1 < ntiles) body(t + 1, st1, st0);
-  }
+  // Query loads must not be mistaken for tile copies by the waits below.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (ntiles > 0) issue(0);
+  if (ntiles > 1) issue(1);
+  if (ntiles > 1)
+    barrier_keep<DPT>();
+  else
+    barrier_keep<0>();
+  for (int t = 0; t < ntiles; ++t) body(t);
   if (!group_a && ntiles > 0) {
     softmax();
-    pv((ntiles - 1) % NSTAGE);
+    pv((ntiles - 1) & (NSTAGE - 1));
   }
 
   // ---- partial result of this split
