@@ -2,12 +2,16 @@
 // the temperature-0 sample, i.e. the argmax; DFlash contributor guide, discosf.com/news/
 // 4742660, "Coding conventions"). Lowest index on ties, bit exact.
 //
-// HBM-bound scan. Each workgroup owns one slice of one row; every thread issues four
-// independent 16-byte loads before touching any of them, so each CU keeps 64 KB in
-// flight. Per vector only a max and one compare are spent; the element index is looked
-// up once, in the winning vector, which is still in registers. Partial (value, index)
-// pairs go to the workspace and the last workgroup of the row, found with a counter,
-// reduces them and restores the counter to zero.
+// HBM-bound scan in two launches:
+//   1. argmax_partial: grid (slices, rows). Every thread issues four independent 16-byte
+//      loads (addresses clamped into the slice, so no load is conditional and all four
+//      are in flight together), keeps only a per-vector max and one compare, and looks up
+//      the element index once, in the winning vector that is still in registers. The
+//      workgroup's (value, index) goes to the workspace (or straight to tok when a row
+//      is a single slice).
+//   2. argmax_final: one wave per row reduces that row's slices.
+// The kernel boundary orders the two, so no atomics, fences or counters are needed and
+// the workspace needs no initialisation.
 #include <climits>
 
 #include "tv_internal.h"
@@ -62,130 +66,116 @@ __device__ __forceinline__ float load_one(const char* row, int e) {
 }
 
 template <bool kF32, bool kVec>
-__global__ __launch_bounds__(kBlock) void argmax_kernel(const char* __restrict__ logits, int V,
-                                                        int64_t row_bytes, int chunks, int chunk_len,
-                                                        int32_t* __restrict__ tok,
-                                                        float* __restrict__ part_v,
-                                                        int* __restrict__ part_i,
-                                                        unsigned* __restrict__ counters) {
+__global__ __launch_bounds__(kBlock) void argmax_partial(const char* __restrict__ logits, int V, int64_t row_bytes,
+                                                         int chunks, int chunk_len, int32_t* __restrict__ tok,
+                                                         float* __restrict__ part_v, int* __restrict__ part_i) {
   constexpr int EPV = kVec ? (kF32 ? 4 : 8) : 1;  // elements per 16-byte load
+  constexpr int ESZ = kF32 ? 4 : 2;
   const int row = blockIdx.y;
   const int c = blockIdx.x;
   const char* rp = logits + (int64_t)row * row_bytes;
   const int begin = c * chunk_len;
   const int end = min(V, begin + chunk_len);
+  const int tid = threadIdx.x;
 
   Best b{-INFINITY, INT_MAX};
+  bool have = false;
   if constexpr (kVec) {
-    // kUnroll independent 16-byte loads per thread, issued before any compare. Thread
-    // tid owns vectors begin + (u * kBlock + tid) * EPV, ascending in u.
-    u32x4 raw[kUnroll];
+    if (end - begin >= EPV) {
+      u32x4 raw[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int e = begin + (u * kBlock + (int)threadIdx.x) * EPV;
-      raw[u] = u32x4{0u, 0u, 0u, 0u};
-      if (e + EPV <= end) raw[u] = *reinterpret_cast<const u32x4*>(rp + (int64_t)e * (kF32 ? 4 : 2));
-    }
-    int bu = -1;
+      for (int u = 0; u < kUnroll; ++u) {
+        const int e = begin + (u * kBlock + tid) * EPV;
+        const int ea = (e + EPV <= end) ? e : begin;  // clamped: always a full vector in the slice
+        raw[u] = *reinterpret_cast<const u32x4*>(rp + (int64_t)ea * ESZ);
+      }
+      int bu = -1;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int e = begin + (u * kBlock + (int)threadIdx.x) * EPV;
-      if (e + EPV <= end) {
+      for (int u = 0; u < kUnroll; ++u) {
+        const int e = begin + (u * kBlock + tid) * EPV;
         float x[8];
         unpack<kF32>(raw[u], x);
         float m = x[0];
 #pragma unroll
         for (int j = 1; j < EPV; ++j) m = fmaxf(m, x[j]);
-        if (bu < 0 || m > b.v) {
+        if (e + EPV <= end && (bu < 0 || m > b.v)) {
           b.v = m;
           bu = u;
         }
       }
-    }
-    // Element index inside the winning vector (first element equal to the maximum).
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (u == bu) {
-        float x[8];
-        unpack<kF32>(raw[u], x);
-        const int e = begin + (u * kBlock + (int)threadIdx.x) * EPV;
+      for (int u = 0; u < kUnroll; ++u) {
+        if (u == bu) {
+          float x[8];
+          unpack<kF32>(raw[u], x);
+          const int e = begin + (u * kBlock + tid) * EPV;
 #pragma unroll
-        for (int j = EPV - 1; j >= 0; --j)
-          if (x[j] == b.v) b.i = e + j;
+          for (int j = EPV - 1; j >= 0; --j)
+            if (x[j] == b.v) b.i = e + j;
+        }
       }
+      have = b.i != INT_MAX;
     }
-    // A vector cut by the end of the row is read element by element (it is the
-    // thread's last and highest-indexed vector, so ascending order is kept).
+    // A vector cut by the end of the row is read element by element; it is the
+    // thread's highest-indexed vector, so ascending order is kept.
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int e = begin + (u * kBlock + (int)threadIdx.x) * EPV;
+      const int e = begin + (u * kBlock + tid) * EPV;
       if (e < end && e + EPV > end) {
         for (int j = e; j < end; ++j) {
           const float x = load_one<kF32>(rp, j);
-          if (b.i == INT_MAX || x > b.v) {
+          if (!have || x > b.v) {
             b.v = x;
             b.i = j;
+            have = true;
           }
         }
       }
     }
-    if (b.i == INT_MAX) b.v = -INFINITY;
   } else {
-    for (int e = begin + (int)threadIdx.x; e < end; e += kBlock) {
+    for (int e = begin + tid; e < end; e += kBlock) {
       const float x = load_one<kF32>(rp, e);
-      if (b.i == INT_MAX || x > b.v) {
+      if (!have || x > b.v) {
         b.v = x;
         b.i = e;
+        have = true;
       }
     }
-    if (b.i == INT_MAX) b.v = -INFINITY;
   }
+  if (!have) b = Best{-INFINITY, INT_MAX};
 
   __shared__ float sv[kBlock / 64];
   __shared__ int si[kBlock / 64];
-  __shared__ bool last;
   b = wave_reduce(b);
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
+  const int wave = tid >> 6;
+  if ((tid & 63) == 0) {
     sv[wave] = b.v;
     si[wave] = b.i;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     Best r{sv[0], si[0]};
     for (int w = 1; w < kBlock / 64; ++w) r = better(r, Best{sv[w], si[w]});
     if (chunks == 1) {
       tok[row] = r.i == INT_MAX ? -1 : r.i;
-      last = false;
     } else {
       part_v[(int64_t)row * chunks + c] = r.v;
       part_i[(int64_t)row * chunks + c] = r.i;
-      __threadfence();
-      last = atomicAdd(&counters[row], 1u) == (unsigned)(chunks - 1);
     }
   }
-  __syncthreads();
-  if (!last) return;
-  // Last workgroup of this row: reduce the row's partials.
-  __threadfence();
+}
+
+// One wave per row: reduce the row's slice results.
+__global__ __launch_bounds__(256) void argmax_final(int N, int chunks, const float* __restrict__ part_v,
+                                                    const int* __restrict__ part_i, int32_t* __restrict__ tok) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= N) return;
   Best r{-INFINITY, INT_MAX};
-  for (int j = threadIdx.x; j < chunks; j += kBlock) {
-    const float v = __hip_atomic_load(&part_v[(int64_t)row * chunks + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int ix = __hip_atomic_load(&part_i[(int64_t)row * chunks + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    r = better(r, Best{v, ix});
-  }
+  for (int j = lane; j < chunks; j += 64)
+    r = better(r, Best{part_v[(int64_t)row * chunks + j], part_i[(int64_t)row * chunks + j]});
   r = wave_reduce(r);
-  if ((threadIdx.x & 63) == 0) {
-    sv[wave] = r.v;
-    si[wave] = r.i;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    Best f{sv[0], si[0]};
-    for (int w = 1; w < kBlock / 64; ++w) f = better(f, Best{sv[w], si[w]});
-    tok[row] = f.i == INT_MAX ? -1 : f.i;
-    atomicExch(&counters[row], 0u);
-  }
+  if (lane == 0) tok[row] = r.i == INT_MAX ? -1 : r.i;
 }
 
 }  // namespace
@@ -203,11 +193,8 @@ ArgmaxPlan argmax_plan(int N, int V, int dtype, bool vec) {
 size_t argmax_workspace_bytes(int N, int V) {
   const ArgmaxPlan p = argmax_plan(N, V, TV_F32, false);  // the most slices of any path
   const size_t parts = (size_t)N * p.chunks;
-  size_t bytes = parts * sizeof(float);
-  bytes = (bytes + 255) / 256 * 256;
+  size_t bytes = (parts * sizeof(float) + 255) / 256 * 256;
   bytes += parts * sizeof(int);
-  bytes = (bytes + 255) / 256 * 256;
-  bytes += (size_t)N * sizeof(unsigned);
   return (bytes + 255) / 256 * 256;
 }
 
@@ -220,28 +207,28 @@ hipError_t launch_argmax(const void* logits, int dtype, int N, int V, int64_t ro
   const size_t parts = (size_t)N * argmax_plan(N, V, TV_F32, false).chunks;
   char* ws = static_cast<char*>(workspace);
   float* part_v = reinterpret_cast<float*>(ws);
-  size_t off = (parts * sizeof(float) + 255) / 256 * 256;
-  int* part_i = reinterpret_cast<int*>(ws + off);
-  off += (parts * sizeof(int) + 255) / 256 * 256;
-  unsigned* counters = reinterpret_cast<unsigned*>(ws + off);
+  int* part_i = reinterpret_cast<int*>(ws + (parts * sizeof(float) + 255) / 256 * 256);
 
   const dim3 grid(p.chunks, N);
   const char* lg = static_cast<const char*>(logits);
   if (dtype == TV_F32) {
     if (vec)
-      hipLaunchKernelGGL((argmax_kernel<true, true>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes,
-                         p.chunks, p.chunk_len, tok, part_v, part_i, counters);
+      hipLaunchKernelGGL((argmax_partial<true, true>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes, p.chunks,
+                         p.chunk_len, tok, part_v, part_i);
     else
-      hipLaunchKernelGGL((argmax_kernel<true, false>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes,
-                         p.chunks, p.chunk_len, tok, part_v, part_i, counters);
+      hipLaunchKernelGGL((argmax_partial<true, false>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes, p.chunks,
+                         p.chunk_len, tok, part_v, part_i);
   } else {
     if (vec)
-      hipLaunchKernelGGL((argmax_kernel<false, true>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes,
-                         p.chunks, p.chunk_len, tok, part_v, part_i, counters);
+      hipLaunchKernelGGL((argmax_partial<false, true>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes, p.chunks,
+                         p.chunk_len, tok, part_v, part_i);
     else
-      hipLaunchKernelGGL((argmax_kernel<false, false>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes,
-                         p.chunks, p.chunk_len, tok, part_v, part_i, counters);
+      hipLaunchKernelGGL((argmax_partial<false, false>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes, p.chunks,
+                         p.chunk_len, tok, part_v, part_i);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.chunks == 1) return e;
+  hipLaunchKernelGGL(argmax_final, dim3((N + 3) / 4), dim3(256), 0, stream, N, p.chunks, part_v, part_i, tok);
   return hipGetLastError();
 }
 

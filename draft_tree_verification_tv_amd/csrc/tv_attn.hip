@@ -92,11 +92,14 @@ __device__ __forceinline__ int swz_v(int r) { return (0xCA60 >> ((r & 3) * 4)) &
 // (global_load_lds_dwordx4): lane i's 16 bytes at gbase + goff land at LDS byte
 // lds + 16*i. No VGPR receives data, so nothing can be overwritten while the copy is in
 // flight; completion is tracked by vmcnt. M0 carries the LDS address and is restored.
+// An LDS-DMA load that follows an SALU write of M0 needs one wait state (s_nop 0), or
+// it may still see the previous M0 and write the wrong LDS block.
 __device__ __forceinline__ void dma16(uint32_t lds, uint32_t goff, const void* gbase) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
       "global_load_lds_dwordx4 %2, %3\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
@@ -316,31 +319,12 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
     }
   };
 
-  // One pipeline step for tile t: tile t+2 starts streaming into LDS; tile t+1 must have
-  // landed before the closing barrier.
-  auto body = [&](int t) __attribute__((always_inline)) {
-    const int kt0 = kbeg + t * KT;
-    const int stage = t & (NSTAGE - 1);
-    if (t + 2 < ntiles) issue(t + 2);
-    if (group_a) {
-      qk(stage);
-      mask(kt0);
-      softmax();
-      pv(stage);
-    } else {
-      if (t > 0) {
-        softmax();
-        pv((t - 1) & (NSTAGE - 1));
-      }
-      qk(stage);
-      mask(kt0);
-    }
+  auto wait_next = [&](int t) __attribute__((always_inline)) {
     if (t + 2 < ntiles)
       barrier_keep<DPT>();
     else
       barrier_keep<0>();
   };
-
   // Query loads must not be mistaken for tile copies by the waits below.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (ntiles > 0) issue(0);
@@ -349,10 +333,32 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
     barrier_keep<DPT>();
   else
     barrier_keep<0>();
-  for (int t = 0; t < ntiles; ++t) body(t);
-  if (!group_a && ntiles > 0) {
-    softmax();
-    pv((ntiles - 1) & (NSTAGE - 1));
+  if (group_a) {
+    for (int t = 0; t < ntiles; ++t) {
+      const int stage = t & (NSTAGE - 1);
+      if (t + 2 < ntiles) issue(t + 2);
+      qk(stage);
+      mask(kbeg + t * KT);
+      softmax();
+      pv(stage);
+      wait_next(t);
+    }
+  } else {
+    for (int t = 0; t < ntiles; ++t) {
+      const int stage = t & (NSTAGE - 1);
+      if (t + 2 < ntiles) issue(t + 2);
+      if (t > 0) {
+        softmax();
+        pv((t - 1) & (NSTAGE - 1));
+      }
+      qk(stage);
+      mask(kbeg + t * KT);
+      wait_next(t);
+    }
+    if (ntiles > 0) {
+      softmax();
+      pv((ntiles - 1) & (NSTAGE - 1));
+    }
   }
 
   // ---- partial result of this split
@@ -460,7 +466,7 @@ AttnPlan attn_plan(int N, int L, int Hq, int Hkv, int num_splits, int num_cus) {
   const int tiles = (p.T + KT - 1) / KT;
   int S = num_splits;
   if (S <= 0) {
-    // One workgroup per CU (the three LDS stages take 106 KB); at least 8 tiles per split
+    // One workgroup per CU (the four LDS stages and the tree masks take 138 KB); at least 8 tiles per split
     // so that partial-output traffic stays small against the KV stream.
     const int units = Hkv * p.RT;
     S = (num_cus + units - 1) / units;

@@ -166,8 +166,8 @@ def argmax_workspace_size(N, V) -> int:
 
 
 def argmax_workspace(N, V, device) -> torch.Tensor:
-    """A zero-filled argmax workspace (the kernels leave it zero-filled after each call)."""
-    return torch.zeros(max(argmax_workspace_size(N, V), 256), dtype=torch.uint8, device=device)
+    """An argmax workspace (per-slice partial results; no initialisation needed)."""
+    return torch.empty(max(argmax_workspace_size(N, V), 256), dtype=torch.uint8, device=device)
 
 
 def argmax(logits, tok=None, workspace=None, V=None, stream=None):

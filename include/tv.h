@@ -98,7 +98,7 @@ int tv_tree_prep(const int32_t* parent, int N, uint64_t* anc, int32_t* depth,
  *   out      bf16 [N][Hq][D] (round to nearest even), contiguous, 16-byte aligned.
  *   lse      optional fp32 [N][Hq], natural-log sum of exp of the scaled scores.
  *   workspace   device scratch of at least tv_tree_attn_workspace_size(...) bytes with
- *               the same num_splits; 256-byte aligned. Contents need no initialisation.
+ *               the same num_splits; 16-byte aligned. Contents need no initialisation.
  * Limits: 1 <= N <= TV_MAX_NODES, L >= 0, D == TV_HEAD_DIM, Hkv >= 1, Hq % Hkv == 0,
  * num_splits in [0, 1024], scale > 0 and finite; (L + N) * kv_stride_t * 2 bytes must stay
  * below 4 GiB (TV_ERR_UNSUPPORTED otherwise). Accumulation is fp32; inputs are never
@@ -117,9 +117,8 @@ int tv_tree_attn(const void* q, const void* k, const void* v, int64_t kv_stride_
  * (float comparison, so -0.0 and +0.0 tie). Rows holding NaN give an unspecified index.
  *   logits   dtype TV_BF16 or TV_F32, row i at base + i*row_stride elements.
  *   tok      int32 [N].
- *   workspace   at least tv_argmax_workspace_size(N, V) bytes, 256-byte aligned. It must
- *               be zero-filled before its first use; every call leaves it zero-filled
- *               again, so one buffer serves any number of calls on one stream.
+ *   workspace   at least tv_argmax_workspace_size(N, V) bytes, 16-byte aligned, used for
+ *               per-slice partial results. Contents need no initialisation.
  * Limits: N >= 1, 1 <= V < 2^31 - 1, row_stride >= V.
  */
 size_t tv_argmax_workspace_size(int N, int V);
