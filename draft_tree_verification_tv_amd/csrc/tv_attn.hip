@@ -236,18 +236,28 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
   f32x16 sc[2];
   bf16x8 pb[4];
 
+  // Scheduling masks for __builtin_amdgcn_sched_group_barrier.
+  constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+
+  // S^T of one tile. The 16 K fragments are read from LDS four MFMAs ahead of their use
+  // (the group barriers pin that order), so the MFMAs issue back to back instead of each
+  // waiting out an LDS round trip.
   auto qk = [&](int stage) __attribute__((always_inline)) {
     const char* Ks = smem + stage * STAGE_B;
     sc[0] = f32x16{};
     sc[1] = f32x16{};
+    bf16x8 a[16];
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) {
+    for (int i = 0; i < 16; ++i) a[i] = *reinterpret_cast<const bf16x8*>(Ks + (i & 1) * 32 * ROWB + koff[i >> 1]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + kb * 32 * ROWB + koff[s8]);
-        sc[kb] = mfma32(a, qf[s8], sc[kb]);
-      }
+    for (int i = 0; i < 16; ++i) sc[i & 1] = mfma32(a[i], qf[i >> 1], sc[i & 1]);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
   };
 
   // Keys past the context: tree keys by ancestry, anything past L+N never.
@@ -303,20 +313,29 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
     }
   };
 
-  // O^T += V^T P^T; V^T fragments come from the row-major V tile via transposed reads.
+  // O^T += V^T P^T; V^T fragments come from the row-major V tile via transposed reads,
+  // issued four MFMAs (eight reads) ahead of their use.
   auto pv = [&](int stage) __attribute__((always_inline)) {
     const char* Vs = smem + stage * STAGE_B + TILE_B;
+    i16x4 lo[16], hi[16];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const char* a0 = Vs + ks * 16 * ROWB + voff[db];
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * ROWB));
-        const i16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = mfma32(__builtin_bit_cast(bf16x8, a), pb[ks], o[db]);
-      }
+    for (int i = 0; i < 16; ++i) {
+      const char* a0 = Vs + (i >> 2) * 16 * ROWB + voff[i & 3];
+      lo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
+      hi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * ROWB));
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const i16x8 a = __builtin_shufflevector(lo[i], hi[i], 0, 1, 2, 3, 4, 5, 6, 7);
+      o[i & 3] = mfma32(__builtin_bit_cast(bf16x8, a), pb[i >> 2], o[i & 3]);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
   };
 
   auto wait_next = [&](int t) __attribute__((always_inline)) {
