@@ -18,21 +18,23 @@
 //     P^T feeds the P.V product as the B operand straight from registers. O^T = V^T P^T
 //     accumulates in 64 fp32 registers per lane.
 //   * Memory pipeline. K and V tiles (64 keys x 128 dims, bf16) are copied HBM -> LDS by
-//     global_load_lds_dwordx4 (no registers involved) into a ring of four stages, two
-//     tiles ahead of the MFMAs; each wave waits only for the tile it needs next and the
-//     barrier drains LDS traffic only, so 64 KB per CU stay in flight. Both tiles are
-//     row-major with a 16-byte-chunk XOR swizzle: K rows are read as 128-bit MFMA A
-//     operands; V is read with ds_read_b64_tr_b16, whose 4x16 in-register transpose hands
-//     each lane four consecutive keys of one head-dim column -- exactly the k-run the P.V
-//     MFMA needs -- so V needs no transposition pass.
-//   * Ping-pong. The waves form two groups that share SIMDs pairwise. Group A runs
-//     QK(t), softmax(t), PV(t); group B runs softmax(t-1), PV(t-1), QK(t). While one wave
-//     of a SIMD is in its VALU-heavy softmax, the other issues MFMAs.
+//     global_load_lds_dwordx4 (no registers involved) into a ring of four stages, three
+//     tiles ahead of their use; each wave waits only for its own copies of the tile it needs
+//     next and the barrier drains LDS traffic only, so up to 96 KB per CU stay in flight.
+//     Both tiles are row-major with a 16-byte-chunk XOR swizzle: K rows are read as 128-bit
+//     MFMA A operands; V is read with ds_read_b64_tr_b16, whose 4x16 in-register transpose
+//     hands each lane four consecutive keys of one head-dim column -- exactly the k-run the
+//     P.V MFMA needs -- so V needs no transposition pass.
+//   * Software pipeline. Every wave walks its keys in 32-key blocks. While it turns block j
+//     into probabilities it already issues the score MFMAs of block j+1 (into the other of
+//     two score buffers), then block j's P.V MFMAs: MFMA and VALU work of one wave overlap,
+//     and the two waves sharing a SIMD fill each other's stalls.
 //   * Softmax. exp2 with the scale folded into one FMA. The reference maximum is raised
-//     only when a tile exceeds it by more than 2^8 (lazy rescaling), so the 64-register
+//     only when a block exceeds it by more than 2^8 (lazy rescaling), so the 64-register
 //     rescale of O is off the common path. Row sums use the unrounded fp32 probabilities
 //     (so the exported log-sum-exp is exact to fp32); P is rounded to bf16 only as the
-//     MFMA operand.
+//     MFMA operand. The two lanes holding a row exchange maxima and sums with
+//     permlane32_swap.
 //   * Tree keys (rows L..L+N-1) are masked with per-node ancestor bitmasks built in LDS by
 //     the workgroups whose range reaches them.
 //   * Work items are remapped so that consecutive ones (the splits of one KV head) land
@@ -144,7 +146,6 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
   const int grp = lane >> 5;
   const int i16 = lane & 15;
   const int g16 = (lane >> 4) & 1;
-  const bool group_a = wave < NW / 2;
 
   const int r = rt * TILE_ROWS + wave * 32 + ql;
   const bool rvalid = r < p.M;
@@ -231,61 +232,75 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  float m_ref = -INFINITY;
-  float lsum = 0.f;
-  f32x16 sc[2];
-  bf16x8 pb[4];
+  float m_ref = -INFINITY;  // reference maximum of the row, log2 domain (scaled)
+  float lsum = 0.f;         // this lane's part of the row sum, relative to m_ref
+  f32x16 sc[2];             // scores of two consecutive 32-key blocks
+  bf16x8 pb[2];             // P^T fragments of the current block (two 16-key steps)
 
   // Scheduling masks for __builtin_amdgcn_sched_group_barrier.
-  constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
-  // S^T of one tile. The 16 K fragments are read from LDS four MFMAs ahead of their use
-  // (the group barriers pin that order), so the MFMAs issue back to back instead of each
-  // waiting out an LDS round trip.
-  auto qk = [&](int stage) __attribute__((always_inline)) {
-    const char* Ks = smem + stage * STAGE_B;
-    sc[0] = f32x16{};
-    sc[1] = f32x16{};
-    bf16x8 a[16];
+  // S^T of 32-key block kb of the tile in `stage` into sc[c]: 8 K fragments, 8 MFMAs.
+  auto qk = [&](int stage, int kb, int c) __attribute__((always_inline)) {
+    const char* Ks = smem + stage * STAGE_B + kb * 32 * ROWB;
+    sc[c] = f32x16{};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) a[i] = *reinterpret_cast<const bf16x8*>(Ks + (i & 1) * 32 * ROWB + koff[i >> 1]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sc[i & 1] = mfma32(a[i], qf[i >> 1], sc[i & 1]);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+    for (int s8 = 0; s8 < 8; ++s8)
+      sc[c] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + koff[s8]), qf[s8], sc[c]);
   };
 
-  // Keys past the context: tree keys by ancestry, anything past L+N never.
-  auto mask = [&](int kt0) __attribute__((always_inline)) {
-    if (kt0 + KT > p.L) {
+  // O^T += V^T P^T over 32-key block kb of the tile in `stage`; V^T fragments come from
+  // the row-major V tile through transposed reads (two per MFMA).
+  auto pv = [&](int stage, int kb) __attribute__((always_inline)) {
+    const char* Vs = smem + stage * STAGE_B + TILE_B + kb * 32 * ROWB;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kt0 + kb * 32 + 8 * (e >> 2) + 4 * grp + (e & 3);
-          bool vis = key < p.L;
-          if (!vis && key < p.T) {
-            const int j = key - p.L;
-            vis = (anc[node * kAncWords + (j >> 6)] >> (j & 63)) & 1ull;
-          }
-          if (!vis) sc[kb][e] = -INFINITY;
-        }
-      }
+    for (int i = 0; i < 8; ++i) {
+      const char* a0 = Vs + (i >> 2) * 16 * ROWB + voff[i & 3];
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * ROWB));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[i & 3] = mfma32(a, pb[i >> 2], o[i & 3]);
     }
   };
 
-  // Online softmax (log2 domain), lazily rescaled; leaves bf16 P^T fragments in pb.
-  auto softmax = [&]() __attribute__((always_inline)) {
-    float mt = -INFINITY;
+  // Keys past the context: tree keys by ancestry, anything past L+N never. The block's 32
+  // keys kb0 .. kb0+31 map to a 32-bit window of the row's ancestor set (bit b <-> node
+  // kb0 + b - L), with context keys (kb0 + b < L) always set; nodes >= N have no ancestor
+  // bit, so keys past L+N come out clear.
+  auto mask = [&](int kb0, int c) __attribute__((always_inline)) {
+    if (kb0 + 32 <= p.L) return;
+    const int d = kb0 - p.L;  // > -32 here
+    const uint64_t* a = anc + node * kAncWords;
+    uint32_t win;
+    if (d >= 0) {
+      const int wi = d >> 6, sh = d & 63;
+      const uint64_t lo = wi < kAncWords ? a[wi] : 0ull;
+      const uint64_t hi = (sh > 32 && wi + 1 < kAncWords) ? a[wi + 1] : 0ull;
+      win = (uint32_t)((lo >> sh) | (sh > 32 ? hi << (64 - sh) : 0ull));
+    } else {
+      win = (uint32_t)((a[0] << (-d)) | ((1ull << (-d)) - 1ull));
+    }
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mt = fmaxf(mt, fmaxf(sc[0][e], sc[1][e]));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    mt *= p.c;
+    for (int e = 0; e < 16; ++e) {
+      const int b = 8 * (e >> 2) + 4 * grp + (e & 3);  // key within the block
+      if (!((win >> b) & 1u)) sc[c][e] = -INFINITY;
+    }
+  };
+
+  // Lazy online-softmax rescale to the maximum of block sc[c]: the reference maximum moves
+  // only when a block exceeds it by more than 2^8. A row's 32 keys are split between lanes
+  // l and l ^ 32, whose maxima permlane32_swap exchanges (max(r0, r1) is the row maximum
+  // in both).
+  auto rescale = [&](int c) __attribute__((always_inline)) {
+    float m0 = fmaxf(sc[c][0], sc[c][1]);
+    float m1 = fmaxf(sc[c][2], sc[c][3]);
+#pragma unroll
+    for (int e = 4; e < 16; e += 4) {
+      m0 = fmaxf(m0, fmaxf(sc[c][e], sc[c][e + 1]));
+      m1 = fmaxf(m1, fmaxf(sc[c][e + 2], sc[c][e + 3]));
+    }
+    const float m = fmaxf(m0, m1);
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    const float mt = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])) * p.c;
     const bool need = mt > m_ref + kRescaleTh;
     if (__any(need)) {
       const float m_new = need ? mt : m_ref;
@@ -295,93 +310,84 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
       for (int i = 0; i < 4; ++i) o[i] *= alpha;
       m_ref = m_new;
     }
+  };
+
+  // Probabilities of block sc[c] relative to m_ref: unrounded fp32 row sums, bf16 P^T
+  // fragments for the P.V MFMAs.
+  auto probs = [&](int c) __attribute__((always_inline)) {
     const float mu = m_ref == -INFINITY ? 0.f : m_ref;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int th = 0; th < 2; ++th) {
+      bf16x2 b[4];
 #pragma unroll
-      for (int th = 0; th < 2; ++th) {
-        bf16x2 b[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][th * 8 + 2 * j], p.c, -mu));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][th * 8 + 2 * j + 1], p.c, -mu));
-          b[j] = __builtin_convertvector((f32x2{p0, p1}), bf16x2);
-          lsum += p0 + p1;
-        }
-        pb[kb * 2 + th] = bf16x8{b[0][0], b[0][1], b[1][0], b[1][1], b[2][0], b[2][1], b[3][0], b[3][1]};
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[c][th * 8 + 2 * j], p.c, -mu));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[c][th * 8 + 2 * j + 1], p.c, -mu));
+        b[j] = __builtin_convertvector((f32x2{p0, p1}), bf16x2);
+        lsum += p0 + p1;
       }
+      pb[th] = bf16x8{b[0][0], b[0][1], b[1][0], b[1][1], b[2][0], b[2][1], b[3][0], b[3][1]};
     }
   };
 
-  // O^T += V^T P^T; V^T fragments come from the row-major V tile via transposed reads,
-  // issued four MFMAs (eight reads) ahead of their use.
-  auto pv = [&](int stage) __attribute__((always_inline)) {
-    const char* Vs = smem + stage * STAGE_B + TILE_B;
-    i16x4 lo[16], hi[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const char* a0 = Vs + (i >> 2) * 16 * ROWB + voff[i & 3];
-      lo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
-      hi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * ROWB));
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const i16x8 a = __builtin_shufflevector(lo[i], hi[i], 0, 1, 2, 3, 4, 5, 6, 7);
-      o[i & 3] = mfma32(__builtin_bit_cast(bf16x8, a), pb[i >> 2], o[i & 3]);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
-  };
-
-  auto wait_next = [&](int t) __attribute__((always_inline)) {
-    if (t + 2 < ntiles)
+  // Barrier closing tile t: tile t+2 has landed; tile t+3 (if any) stays in flight.
+  auto wait_step = [&](int t) __attribute__((always_inline)) {
+    if (t + 3 < ntiles)
       barrier_keep<DPT>();
     else
       barrier_keep<0>();
   };
-  // Query loads must not be mistaken for tile copies by the waits below.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (ntiles > 0) issue(0);
-  if (ntiles > 1) issue(1);
-  if (ntiles > 1)
+
+  // Tiles whose 64 keys all precede L need no mask.
+  const int nplain = p.L > kbeg ? min(ntiles, (p.L - kbeg) / KT) : 0;
+
+  // Sub-step over 32-key block (t, kb) with a successor block (tn, kb ^ 1): the
+  // successor's score MFMAs, this block's softmax and this block's P.V MFMAs form one
+  // scheduling region, so the compiler interleaves MFMAs with the softmax VALU work; then
+  // the successor is masked (if it reaches past the context) and the running maximum
+  // updated. The score buffer index equals kb.
+  auto sub = [&](int t, auto kbc, int tn) __attribute__((always_inline)) {
+    constexpr int kb = decltype(kbc)::value;
+    constexpr int kbn = kb ^ 1;
+    qk(tn & (NSTAGE - 1), kbn, kbn);
+    probs(kb);
+    pv(t & (NSTAGE - 1), kb);
+    if (tn >= nplain) mask(kbeg + tn * KT + kbn * 32, kbn);
+    rescale(kbn);
+  };
+
+  // ---- prologue: tiles 0, 1, 2 start streaming; tiles 0 and 1 must land.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // query loads are not tile copies
+  for (int t = 0; t < 3 && t < ntiles; ++t) issue(t);
+  if (ntiles > 2)
     barrier_keep<DPT>();
   else
     barrier_keep<0>();
-  if (group_a) {
-    for (int t = 0; t < ntiles; ++t) {
-      const int stage = t & (NSTAGE - 1);
-      if (t + 2 < ntiles) issue(t + 2);
-      qk(stage);
-      mask(kbeg + t * KT);
-      softmax();
-      pv(stage);
-      wait_next(t);
-    }
-  } else {
-    for (int t = 0; t < ntiles; ++t) {
-      const int stage = t & (NSTAGE - 1);
-      if (t + 2 < ntiles) issue(t + 2);
-      if (t > 0) {
-        softmax();
-        pv((t - 1) & (NSTAGE - 1));
-      }
-      qk(stage);
-      mask(kbeg + t * KT);
-      wait_next(t);
-    }
-    if (ntiles > 0) {
-      softmax();
-      pv((ntiles - 1) & (NSTAGE - 1));
-    }
+  qk(0, 0, 0);
+  if (nplain == 0) mask(kbeg, 0);
+  rescale(0);
+
+  // Tile t: block 0 (successor: block 1 of tile t), block 1 (successor: block 0 of tile
+  // t+1); the barrier after each tile guarantees tile t+2 and keeps tile t+3 in flight.
+  // Stage reuse: tile t+3 overwrites tile t-1, whose last reads were in tile t-1's blocks.
+  for (int t = 0; t + 1 < ntiles; ++t) {
+    if (t + 3 < ntiles) issue(t + 3);
+    sub(t, std::integral_constant<int, 0>{}, t);
+    sub(t, std::integral_constant<int, 1>{}, t + 1);
+    wait_step(t);
+  }
+  {
+    const int t = ntiles - 1;
+    sub(t, std::integral_constant<int, 0>{}, t);
+    probs(1);
+    pv(t & (NSTAGE - 1), 1);
   }
 
   // ---- partial result of this split
-  lsum += __shfl_xor(lsum, 32);
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+    lsum = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   const float lse2 = lsum > 0.f ? m_ref + __log2f(lsum) : -INFINITY;
   if (rvalid) {
