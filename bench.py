@@ -8,8 +8,8 @@ calls, each on its own KV buffer (64 buffers, 34.4 GB, far beyond the 256 MB Inf
 Cache), then one argmax over the logits and one acceptance walk.
 
 Reported ``value``: microseconds per tree-verify call = mean attention time per
-layer-equivalent call + argmax time + acceptance time (HIP events on the stream the
-kernels run on). ``roofline`` relates the attention call's algorithmic bytes (K + V + Q +
+layer-equivalent call + the time of the argmax-and-accept call (HIP events on the stream
+the kernels run on). ``roofline`` relates the attention call's algorithmic bytes (K + V + Q +
 out) to its measured duration against the 8 TB/s HBM peak. ``cpu_baseline`` times the
 float64 CPU oracle on whole verify calls of the same workload (about 10 s of CPU work).
 
@@ -125,12 +125,10 @@ def main():
                          stream=stream)
         if ev:
             ev[1].record(stream)
-        tv.argmax(logits, tok=tok, workspace=am_ws, stream=stream)
+        # argmax over the vocabulary and the accept walk: one call, two launches
+        tv.argmax_accept(logits, parent, draft, tok=tok, out=acc, workspace=am_ws, stream=stream)
         if ev:
             ev[2].record(stream)
-        tv.accept(parent, draft, tok, out=acc, stream=stream)
-        if ev:
-            ev[3].record(stream)
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
@@ -147,7 +145,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -157,13 +155,10 @@ def main():
     wall = time.perf_counter() - t0
 
     attn_ms = np.array([e[0].elapsed_time(e[1]) for e in events]) / layers
-    argmax_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
-    accept_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
-    step_ms = np.array([e[0].elapsed_time(e[3]) for e in events])
+    tokens_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
     t_attn_us = float(np.median(attn_ms) * 1e3)
-    t_argmax_us = float(np.median(argmax_ms) * 1e3)
-    t_accept_us = float(np.median(accept_ms) * 1e3)
-    call_us = t_attn_us + t_argmax_us + t_accept_us
+    t_tokens_us = float(np.median(tokens_ms) * 1e3)
+    call_us = t_attn_us + t_tokens_us
     ms_per_step = wall * 1e3 / args.steps
 
     kv_bytes = 2 * T * Hkv * D * 2
@@ -172,15 +167,14 @@ def main():
     achieved = algo_bytes / (t_attn_us * 1e-6) / 1e9
     kv_gbps = kv_bytes / (t_attn_us * 1e-6) / 1e9
     log(f"attn {t_attn_us:.1f} us/call ({kv_gbps:.0f} GB/s KV, {kv_gbps / HBM_PEAK_GBS:.1%} of peak), "
-        f"argmax {t_argmax_us:.1f} us, accept {t_accept_us:.1f} us, step {ms_per_step:.2f} ms")
+        f"argmax+accept {t_tokens_us:.1f} us, step {ms_per_step:.2f} ms")
 
     parity = None
     if not args.no_check:
         import oracle
         log("parity re-check on KV buffer 0 (argmax, accept, 2 q heads of attention)")
         tv.tree_attn(q, K[0], Vc[0], parent, L=L, scale=w.scale, num_splits=args.splits, out=out, workspace=ws)
-        tv.argmax(logits, tok=tok, workspace=am_ws)
-        tv.accept(parent, draft, tok, out=acc)
+        tv.argmax_accept(logits, parent, draft, tok=tok, out=acc, workspace=am_ws)
         torch.cuda.synchronize()
         sub = [0, Hq - 1]
         qf = oracle.bf16_bits_to_f64(w.q[:, sub])
@@ -192,9 +186,12 @@ def main():
         excess = float((np.abs(got - ref) - (1e-2 + 2e-2 * np.abs(ref))).max())
         rel = float((np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)).max())
         etok = oracle.argmax_rows(oracle.bf16_bits_to_f64(w.logits))
-        eln = oracle.accept(w.parent, w.draft, etok)[0]
+        eln, enodes, etoks, ebonus = oracle.accept(w.parent, w.draft, etok)
+        got_nodes = acc[1].cpu().numpy()
+        accept_ok = (int(acc[0].item()) == eln and got_nodes[:eln].tolist() == enodes.tolist()
+                     and acc[2].cpu().numpy()[:eln].tolist() == etoks.tolist() and int(acc[3].item()) == ebonus)
         parity = {"attn_max_abs": err, "attn_row_rel": rel, "argmax_exact": bool((tok.cpu().numpy() == etok).all()),
-                  "accept_exact": int(acc[0].item()) == eln, "accept_len": eln}
+                  "accept_exact": bool(accept_ok), "accept_len": int(eln)}
         ok = excess <= 0 and rel <= 2e-2 and parity["argmax_exact"] and parity["accept_exact"]
         log(f"parity {'OK' if ok else 'FAILED'}: {parity}")
         if not ok:
@@ -246,8 +243,8 @@ def main():
                                "KV buffers + argmax + accept per step",
                    "kv_len": L, "nodes": N, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "vocab": V,
                    "layers_per_step": layers, "parallelism": "none (1 GPU)"},
-        "breakdown_us": {"attn_per_call": round(t_attn_us, 2), "argmax": round(t_argmax_us, 2),
-                         "accept": round(t_accept_us, 2), "attn_p10": round(float(np.percentile(attn_ms, 10) * 1e3), 2),
+        "breakdown_us": {"attn_per_call": round(t_attn_us, 2), "argmax_accept": round(t_tokens_us, 2),
+                         "attn_p10": round(float(np.percentile(attn_ms, 10) * 1e3), 2),
                          "attn_p90": round(float(np.percentile(attn_ms, 90) * 1e3), 2)},
         "kv_gbps": round(kv_gbps, 1),
         "kv_hbm_frac": round(kv_gbps / HBM_PEAK_GBS, 4),

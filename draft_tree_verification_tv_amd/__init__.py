@@ -12,6 +12,7 @@ from .tv import (  # noqa: F401
     abi_version,
     accept,
     argmax,
+    argmax_accept,
     argmax_workspace,
     argmax_workspace_size,
     lib,

@@ -116,4 +116,19 @@ int tv_accept(const int32_t* parent, const int32_t* draft, const int32_t* tok, i
                                      dev_error, static_cast<hipStream_t>(stream)));
 }
 
+int tv_argmax_accept(const void* logits, int dtype, int N, int V, int64_t row_stride, const int32_t* parent,
+                     const int32_t* draft, int32_t* tok, int32_t* accept_len, int32_t* accept_nodes,
+                     int32_t* accept_tokens, int32_t* bonus, void* workspace, size_t workspace_bytes,
+                     int32_t* dev_error, void* stream) {
+  if (!logits || !tok || !parent || !draft || !accept_len || !accept_nodes || !accept_tokens)
+    return TV_ERR_INVALID_ARG;
+  if (N < 1 || N > TV_MAX_NODES || V < 1 || V >= INT32_MAX || row_stride < V) return TV_ERR_INVALID_ARG;
+  if (dtype != TV_BF16 && dtype != TV_F32) return TV_ERR_INVALID_ARG;
+  const size_t need = tv::argmax_workspace_bytes(N, V);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return TV_ERR_WORKSPACE;
+  return status_of(tv::launch_argmax_accept(logits, dtype, N, V, row_stride, parent, draft, tok, accept_len,
+                                            accept_nodes, accept_tokens, bonus, workspace, dev_error,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -13,6 +13,7 @@
 // The kernel boundary orders the two, so no atomics, fences or counters are needed and
 // the workspace needs no initialisation.
 #include <climits>
+#include <cmath>
 
 #include "tv_internal.h"
 
@@ -178,6 +179,59 @@ __global__ __launch_bounds__(256) void argmax_final(int N, int chunks, const flo
   if (lane == 0) tok[row] = r.i == INT_MAX ? -1 : r.i;
 }
 
+// One workgroup finishes the verify step: thread i reduces node row i's slice results to
+// the row argmax (loads batched eight slices at a time, indices clamped so that no load is
+// conditional; a repeated (value, index) pair cannot change the result), keeps the tokens
+// in LDS and runs the acceptance walk on them (the walk of tv_accept). The tree
+// preprocessing and the draft loads are issued first so that their latency overlaps the
+// reduction. With a single slice per row the slice kernel already wrote tok.
+constexpr int kFuseThreads = kMaxNodes;
+
+__global__ __launch_bounds__(kFuseThreads) void argmax_accept_kernel(
+    int N, int chunks, const float* __restrict__ part_v, const int* __restrict__ part_i, int32_t* tok,
+    const int32_t* __restrict__ parent, const int32_t* __restrict__ draft, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ accept_nodes, int32_t* __restrict__ accept_tokens, int32_t* __restrict__ bonus,
+    int32_t* dev_error) {
+  __shared__ uint64_t anc[kMaxNodes * kAncWords];
+  __shared__ int par[kMaxNodes];
+  __shared__ int jmp[kMaxNodes];
+  __shared__ uint64_t okw[kAncWords];
+  __shared__ uint32_t red[kFuseThreads / 64];
+  __shared__ int32_t tok_s[kMaxNodes];
+  const int i = threadIdx.x;
+  const int draft_i = i < N ? draft[i] : 0;
+  tree_prep_lds(parent, N, anc, par, jmp, dev_error);
+
+  if (i < N) {
+    int32_t t;
+    if (chunks > 1) {
+      const float* pv = part_v + (int64_t)i * chunks;
+      const int* pi = part_i + (int64_t)i * chunks;
+      Best b{-INFINITY, INT_MAX};
+      for (int j0 = 0; j0 < chunks; j0 += 8) {
+        float v[8];
+        int ix[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int j = min(j0 + u, chunks - 1);
+          v[u] = pv[j];
+          ix[u] = pi[j];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) b = better(b, Best{v[u], ix[u]});
+      }
+      t = b.i == INT_MAX ? -1 : b.i;
+      tok[i] = t;
+    } else {
+      t = tok[i];
+    }
+    tok_s[i] = t;
+  }
+  __syncthreads();
+  accept_block<kFuseThreads>(anc, par, tok_s, draft_i, N, okw, red, accept_len, accept_nodes, accept_tokens,
+                             bonus);
+}
+
 }  // namespace
 
 ArgmaxPlan argmax_plan(int N, int V, int dtype, bool vec) {
@@ -198,17 +252,9 @@ size_t argmax_workspace_bytes(int N, int V) {
   return (bytes + 255) / 256 * 256;
 }
 
-hipError_t launch_argmax(const void* logits, int dtype, int N, int V, int64_t row_stride, int32_t* tok,
-                         void* workspace, hipStream_t stream) {
-  const int esize = dtype == TV_F32 ? 4 : 2;
-  const int64_t row_bytes = row_stride * esize;
-  const bool vec = ((uintptr_t)logits % 16 == 0) && (row_bytes % 16 == 0);
-  const ArgmaxPlan p = argmax_plan(N, V, dtype, vec);
-  const size_t parts = (size_t)N * argmax_plan(N, V, TV_F32, false).chunks;
-  char* ws = static_cast<char*>(workspace);
-  float* part_v = reinterpret_cast<float*>(ws);
-  int* part_i = reinterpret_cast<int*>(ws + (parts * sizeof(float) + 255) / 256 * 256);
-
+hipError_t launch_argmax_partial(const void* logits, int dtype, int N, int V, int64_t row_bytes, bool vec,
+                                 const ArgmaxPlan& p, int32_t* tok, float* part_v, int* part_i,
+                                 hipStream_t stream) {
   const dim3 grid(p.chunks, N);
   const char* lg = static_cast<const char*>(logits);
   if (dtype == TV_F32) {
@@ -226,9 +272,46 @@ hipError_t launch_argmax(const void* logits, int dtype, int N, int V, int64_t ro
       hipLaunchKernelGGL((argmax_partial<false, false>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes, p.chunks,
                          p.chunk_len, tok, part_v, part_i);
   }
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax(const void* logits, int dtype, int N, int V, int64_t row_stride, int32_t* tok,
+                         void* workspace, hipStream_t stream) {
+  const int esize = dtype == TV_F32 ? 4 : 2;
+  const int64_t row_bytes = row_stride * esize;
+  const bool vec = ((uintptr_t)logits % 16 == 0) && (row_bytes % 16 == 0);
+  const ArgmaxPlan p = argmax_plan(N, V, dtype, vec);
+  const size_t parts = (size_t)N * argmax_plan(N, V, TV_F32, false).chunks;
+  char* ws = static_cast<char*>(workspace);
+  float* part_v = reinterpret_cast<float*>(ws);
+  int* part_i = reinterpret_cast<int*>(ws + (parts * sizeof(float) + 255) / 256 * 256);
+  hipError_t e = launch_argmax_partial(logits, dtype, N, V, row_bytes, vec, p, tok, part_v, part_i, stream);
   if (e != hipSuccess || p.chunks == 1) return e;
   hipLaunchKernelGGL(argmax_final, dim3((N + 3) / 4), dim3(256), 0, stream, N, p.chunks, part_v, part_i, tok);
+  return hipGetLastError();
+}
+
+}  // namespace tv
+
+namespace tv {
+
+hipError_t launch_argmax_accept(const void* logits, int dtype, int N, int V, int64_t row_stride,
+                                const int32_t* parent, const int32_t* draft, int32_t* tok,
+                                int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
+                                int32_t* bonus, void* workspace, int32_t* dev_error,
+                                hipStream_t stream) {
+  const int esize = dtype == TV_F32 ? 4 : 2;
+  const int64_t row_bytes = row_stride * esize;
+  const bool vec = ((uintptr_t)logits % 16 == 0) && (row_bytes % 16 == 0);
+  const ArgmaxPlan p = argmax_plan(N, V, dtype, vec);
+  const size_t parts = (size_t)N * argmax_plan(N, V, TV_F32, false).chunks;
+  char* ws = static_cast<char*>(workspace);
+  float* part_v = reinterpret_cast<float*>(ws);
+  int* part_i = reinterpret_cast<int*>(ws + (parts * sizeof(float) + 255) / 256 * 256);
+  hipError_t e = launch_argmax_partial(logits, dtype, N, V, row_bytes, vec, p, tok, part_v, part_i, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(argmax_accept_kernel, dim3(1), dim3(kFuseThreads), 0, stream, N, p.chunks, part_v, part_i,
+                     tok, parent, draft, accept_len, accept_nodes, accept_tokens, bonus, dev_error);
   return hipGetLastError();
 }
 

@@ -78,6 +78,83 @@ __device__ __forceinline__ int anc_popcount(const uint64_t* anc, int i) {
   return c;
 }
 
+// Largest 32-bit key over the block (kThreads threads); `red` holds kThreads/64 words.
+template <int kThreads>
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t x, uint32_t* red) {
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = __shfl_xor(x, off);
+    x = o > x ? o : x;
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = x;
+  __syncthreads();
+  uint32_t r = red[0];
+  for (int w = 1; w < kThreads / 64; ++w) r = red[w] > r ? red[w] : r;
+  __syncthreads();
+  return r;
+}
+
+// Longest accepted path of one tree, computed by one workgroup of kThreads >= N threads
+// after tree_prep_lds has filled anc/par. Thread i handles node i: `draft_i` is draft[i]
+// and tok[i] (any address space) the target's argmax for node i.
+//   ok[i]       draft[i] == tok[i];
+//   accepted    every node on the path from the prefix to i is ok (anc[i] within ok);
+//   result      the deepest accepted node, ties to the lowest index; its path in
+//               root-to-leaf (= ascending index) order, then -1 padding;
+//   bonus       tok of the lowest-index child of the end node (of the prefix when nothing
+//               is accepted), -1 when there is none.
+template <int kThreads>
+__device__ __forceinline__ void accept_block(const uint64_t* anc, const int* par, const int32_t* tok, int draft_i,
+                                             int N, uint64_t* okw, uint32_t* red, int32_t* accept_len,
+                                             int32_t* accept_nodes, int32_t* accept_tokens, int32_t* bonus) {
+  const int i = threadIdx.x;
+  const int wave = i >> 6;
+  const bool ok = (i < N) && (draft_i == tok[i]);
+  const uint64_t ball = __ballot(ok);
+  if ((i & 63) == 0 && wave < kAncWords) okw[wave] = ball;
+  __syncthreads();
+
+  bool elig = i < N;
+  if (elig) {
+#pragma unroll
+    for (int w = 0; w < kAncWords; ++w) elig = elig && ((anc[i * kAncWords + w] & ~okw[w]) == 0ull);
+  }
+  // Longest path first, then the lowest end index: key = depth << 16 | (0xFFFF - i).
+  const uint32_t key = elig ? ((uint32_t)anc_popcount(anc, i) << 16) | (0xFFFFu - (uint32_t)i) : 0u;
+  const uint32_t best = block_max_u32<kThreads>(key, red);
+  const int len = (int)(best >> 16);
+  const int end = best ? (int)(0xFFFFu - (best & 0xFFFFu)) : -1;
+
+  if (i < N) {
+    bool on_path = false;
+    int pos = 0;
+    if (end >= 0) {
+      const int w = i >> 6, b = i & 63;
+      on_path = (anc[end * kAncWords + w] >> b) & 1ull;
+      // Nodes on the path in ascending index order are in root-to-leaf order because
+      // parent[i] < i.
+      for (int x = 0; x < w; ++x) pos += __popcll(anc[end * kAncWords + x]);
+      pos += __popcll(anc[end * kAncWords + w] & ((1ull << b) - 1ull));
+    }
+    if (on_path) {
+      accept_nodes[pos] = i;
+      accept_tokens[pos] = draft_i;
+    }
+    if (i >= len) {
+      accept_nodes[i] = -1;
+      accept_tokens[i] = -1;
+    }
+  }
+
+  const uint32_t child = (i < N && par[i] == end) ? (uint32_t)(0xFFFFu - (uint32_t)i) : 0u;
+  const uint32_t first_child = block_max_u32<kThreads>(child, red);
+  if (i == 0) {
+    *accept_len = len;
+    if (bonus) *bonus = first_child ? tok[0xFFFFu - first_child] : -1;
+  }
+}
+
+
 // Launch helpers implemented in the .hip files. Return hipSuccess or the launch error.
 hipError_t launch_tree_prep(const int32_t* parent, int N, uint64_t* anc, int32_t* depth,
                             int32_t* dev_error, hipStream_t stream);
@@ -93,6 +170,11 @@ ArgmaxPlan argmax_plan(int N, int V, int dtype, bool vec);
 size_t argmax_workspace_bytes(int N, int V);
 hipError_t launch_argmax(const void* logits, int dtype, int N, int V, int64_t row_stride,
                          int32_t* tok, void* workspace, hipStream_t stream);
+hipError_t launch_argmax_accept(const void* logits, int dtype, int N, int V, int64_t row_stride,
+                                const int32_t* parent, const int32_t* draft, int32_t* tok,
+                                int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
+                                int32_t* bonus, void* workspace, int32_t* dev_error,
+                                hipStream_t stream);
 
 struct AttnPlan {
   int G, M;        // q heads per KV head; stacked rows per KV head (G * N)

@@ -31,20 +31,6 @@ __global__ __launch_bounds__(kBlock) void tree_prep_kernel(const int32_t* __rest
   }
 }
 
-__device__ __forceinline__ uint32_t block_max_u32(uint32_t x, uint32_t* red) {
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t o = __shfl_xor(x, off);
-    x = o > x ? o : x;
-  }
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = x;
-  __syncthreads();
-  uint32_t r = red[0];
-  for (int w = 1; w < kBlock / 64; ++w) r = red[w] > r ? red[w] : r;
-  __syncthreads();
-  return r;
-}
-
 __global__ __launch_bounds__(kBlock) void accept_kernel(const int32_t* __restrict__ parent,
                                                         const int32_t* __restrict__ draft,
                                                         const int32_t* __restrict__ tok, int N,
@@ -58,57 +44,10 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(const int32_t* __restric
   __shared__ int jmp[kMaxNodes];
   __shared__ uint64_t okw[kAncWords];
   __shared__ uint32_t red[kBlock / 64];
-
-  tree_prep_lds(parent, N, anc, par, jmp, dev_error);
   const int i = threadIdx.x;
-  const int wave = i >> 6;
-
-  // Match mask: bit i set when node i's draft equals the target's argmax.
-  const bool ok = (i < N) && (draft[i] == tok[i]);
-  const uint64_t ball = __ballot(ok);
-  if ((i & 63) == 0) okw[wave] = ball;
-  __syncthreads();
-
-  // A node is accepted when every node on its path matches: anc[i] is a subset of okw.
-  bool elig = i < N;
-  if (elig) {
-#pragma unroll
-    for (int w = 0; w < kAncWords; ++w) elig = elig && ((anc[i * kAncWords + w] & ~okw[w]) == 0ull);
-  }
-  // Longest path first, then the lowest end index: key = depth << 16 | (0xFFFF - i).
-  const uint32_t key = elig ? ((uint32_t)anc_popcount(anc, i) << 16) | (0xFFFFu - (uint32_t)i) : 0u;
-  const uint32_t best = block_max_u32(key, red);
-  const int len = (int)(best >> 16);
-  const int end = best ? (int)(0xFFFFu - (best & 0xFFFFu)) : -1;
-
-  if (i < N) {
-    bool on_path = false;
-    int pos = 0;
-    if (end >= 0) {
-      const int w = i >> 6, b = i & 63;
-      on_path = (anc[end * kAncWords + w] >> b) & 1ull;
-      // Nodes on the path in ascending index order are in root-to-leaf order
-      // because parent[i] < i.
-      for (int x = 0; x < w; ++x) pos += __popcll(anc[end * kAncWords + x]);
-      pos += __popcll(anc[end * kAncWords + w] & ((1ull << b) - 1ull));
-    }
-    if (on_path) {
-      accept_nodes[pos] = i;
-      accept_tokens[pos] = draft[i];
-    }
-    if (i >= len) {
-      accept_nodes[i] = -1;
-      accept_tokens[i] = -1;
-    }
-  }
-
-  // Bonus: the target's argmax at the first child of the path's last node.
-  const uint32_t child = (i < N && par[i] == end) ? (uint32_t)(0xFFFFu - (uint32_t)i) : 0u;
-  const uint32_t first_child = block_max_u32(child, red);
-  if (i == 0) {
-    *accept_len = len;
-    if (bonus) *bonus = first_child ? tok[0xFFFFu - first_child] : -1;
-  }
+  const int draft_i = i < N ? draft[i] : 0;
+  tree_prep_lds(parent, N, anc, par, jmp, dev_error);
+  accept_block<kBlock>(anc, par, tok, draft_i, N, okw, red, accept_len, accept_nodes, accept_tokens, bonus);
 }
 
 }  // namespace

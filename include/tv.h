@@ -17,6 +17,7 @@
  *   tv_tree_attn  tree-masked attention of N nodes over a bf16 KV cache
  *   tv_argmax     row argmax of the target logits                      (bit exact)
  *   tv_accept     longest accepted root-to-node path                   (bit exact)
+ *   tv_argmax_accept   the two above in one call
  *
  * Conventions shared by every call
  *   - Pointers are DEVICE pointers unless the name ends in _host. The caller owns every
@@ -140,6 +141,23 @@ int tv_argmax(const void* logits, int dtype, int N, int V, int64_t row_stride,
 int tv_accept(const int32_t* parent, const int32_t* draft, const int32_t* tok, int N,
               int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
               int32_t* bonus, int32_t* dev_error, void* stream);
+
+/*
+ * Argmax and acceptance in one call: tok = row argmax of the logits (exactly as
+ * tv_argmax), then the longest accepted path on those tokens (exactly as tv_accept). Both
+ * steps of greedy verification follow the passages cited for tv_argmax and tv_accept; one
+ * workgroup finishes the row reductions and walks the tree, so the pair costs one launch
+ * fewer than two separate calls and tok never leaves the chip before the walk.
+ *   logits, dtype, V, row_stride, tok, workspace   as for tv_argmax (same workspace size).
+ *   parent, draft, accept_len, accept_nodes, accept_tokens, bonus, dev_error   as for
+ *            tv_accept.
+ * Limits: 1 <= N <= TV_MAX_NODES and the limits of tv_argmax.
+ */
+int tv_argmax_accept(const void* logits, int dtype, int N, int V, int64_t row_stride,
+                     const int32_t* parent, const int32_t* draft, int32_t* tok,
+                     int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
+                     int32_t* bonus, void* workspace, size_t workspace_bytes,
+                     int32_t* dev_error, void* stream);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_documented_calls():
     names = declared_functions()
-    for n in ("tv_tree_attn", "tv_argmax", "tv_accept", "tv_tree_prep", "tv_abi_version",
+    for n in ("tv_tree_attn", "tv_argmax", "tv_accept", "tv_argmax_accept", "tv_tree_prep", "tv_abi_version",
               "tv_validate_tree_host"):
         assert n in names
     assert set(names) == set(tv.EXPORTS)
@@ -118,6 +118,33 @@ def test_argmax_rejects(args, status):
 ])
 def test_accept_rejects(args, status):
     assert tv.lib().tv_accept(*args, None, None, None) == status
+
+
+# tv_argmax_accept(logits, dtype, N, V, row_stride, parent, draft, tok, len, nodes, tokens,
+#                  bonus, workspace, workspace_bytes, dev_error, stream)
+@pytest.mark.parametrize("args,status", [
+    ((None, 0, 4, 100, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), 1),
+    ((FAKE, 0, 4, 100, 100, None, FAKE, FAKE, FAKE, FAKE, FAKE), 1),
+    ((FAKE, 0, 4, 100, 100, FAKE, None, FAKE, FAKE, FAKE, FAKE), 1),
+    ((FAKE, 0, 4, 100, 100, FAKE, FAKE, None, FAKE, FAKE, FAKE), 1),
+    ((FAKE, 0, 4, 100, 100, FAKE, FAKE, FAKE, None, FAKE, FAKE), 1),
+    ((FAKE, 0, 4, 100, 100, FAKE, FAKE, FAKE, FAKE, None, FAKE), 1),
+    ((FAKE, 0, 4, 100, 100, FAKE, FAKE, FAKE, FAKE, FAKE, None), 1),
+    ((FAKE, 0, 257, 100, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), 1),
+    ((FAKE, 0, 0, 100, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), 1),
+    ((FAKE, 3, 4, 100, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), 1),
+    ((FAKE, 0, 4, 100, 99, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), 1),
+])
+def test_argmax_accept_rejects(args, status):
+    assert tv.lib().tv_argmax_accept(*args, None, FAKE, 1 << 30, None, None) == status
+
+
+def test_argmax_accept_workspace_checks():
+    L = tv.lib()
+    args = (FAKE, 0, 4, 100, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert L.tv_argmax_accept(*args, None, 1 << 30, None, None) == 4
+    assert L.tv_argmax_accept(*args, FAKE, 8, None, None) == 4
+    assert L.tv_argmax_accept(*args, ctypes.c_void_p(0x10008), 1 << 30, None, None) == 4
 
 
 def test_tree_prep_rejects():

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from tests.gpu_util import check_attention, dev_bf16, dev_i32, note
-from workloads import (accept_trial, chain_parent, kary_bfs_parent, make, random_tree_parent,
+from workloads import (accept_trial, bf16_bits_from_f32, chain_parent, kary_bfs_parent, make, random_tree_parent,
                        rng_for, tie_rows)
 
 pytestmark = pytest.mark.gpu
@@ -324,3 +324,75 @@ def test_verify_pipeline(name, trial):
     assert nodes.cpu().numpy()[:eln].tolist() == enodes.tolist()
     assert toks.cpu().numpy()[:eln].tolist() == etoks.tolist()
     assert bonus.item() == ebonus
+
+
+# ------------------------------------------------------ a5 + a6 in one call
+
+
+def check_argmax_accept(logits_dev, parent, draft, etok, label):
+    tok, (ln, nodes, toks, bonus) = tv.argmax_accept(logits_dev, dev_i32(parent), dev_i32(draft))
+    torch.cuda.synchronize()
+    assert np.array_equal(tok.cpu().numpy(), etok), label
+    e_ln, e_nodes, e_toks, e_bonus = oracle.accept(parent, draft, etok)
+    ln = ln.item()
+    nodes, toks = nodes.cpu().numpy(), toks.cpu().numpy()
+    assert ln == e_ln, label
+    assert nodes[:ln].tolist() == e_nodes.tolist(), label
+    assert toks[:ln].tolist() == e_toks.tolist(), label
+    assert (nodes[ln:] == -1).all() and (toks[ln:] == -1).all(), label
+    assert bonus.item() == e_bonus, label
+    return ln
+
+
+@pytest.mark.parametrize("name,trials", [("tiny_chain", 6), ("branch_8k", 12), ("wide_tree", 3),
+                                         ("max_256k", 2), ("budget22", 4), ("decode_1node", 2)])
+def test_argmax_accept_workloads(name, trials):
+    """Fused argmax + walk equals the oracle's argmax and walk (and the planted length)."""
+    for trial in range(trials):
+        w = make(name, trial, parts=("tree", "logits"))
+        note(f"argmax_accept {name} trial {trial}")
+        if w.logits_dtype == "bf16":
+            lg, etok = dev_bf16(w.logits), oracle.argmax_rows(oracle.bf16_bits_to_f64(w.logits))
+        else:
+            lg, etok = torch.from_numpy(w.logits).cuda(), oracle.argmax_rows(w.logits.astype(np.float64))
+        ln = check_argmax_accept(lg, w.parent, w.draft, etok, f"{name}/{trial}")
+        assert ln == w.planted_len
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V,stride", [(1, 1), (4096, 4096), (8192, 8192), (8193, 8200), (152064, 152064),
+                                      (152063, 152067)])
+def test_argmax_accept_small_vocab_trees(dtype, V, stride):
+    """Random trees with draft tokens drawn from the top few logits, so paths and ties vary;
+    one and several slices per row, aligned and unaligned rows."""
+    rng = np.random.default_rng(V + 7 * stride)
+    for case in range(3):
+        n = [1, 37, 256][case]
+        parent = np.array([-1] + [int(rng.integers(-1, i)) for i in range(1, n)], dtype=np.int32)
+        x = rng.standard_normal((n, stride)).astype(np.float32)
+        x[:, : min(V, 3)] += 5.0                     # a few large candidates per row
+        if V >= 3 and case == 1:
+            x[::3, 1] = x[::3, 0]                    # exact ties at the maximum
+        xv = x if dtype == "f32" else None
+        if dtype == "bf16":
+            bits = bf16_bits_from_f32(x)
+            etok = oracle.argmax_rows(oracle.bf16_bits_to_f64(bits[:, :V]))
+            lg = dev_bf16(bits)[:, :V]
+        else:
+            etok = oracle.argmax_rows(xv[:, :V].astype(np.float64))
+            lg = torch.from_numpy(xv).cuda()[:, :V]
+        draft = np.where(rng.random(n) < 0.7, etok, rng.integers(0, max(V, 1), n)).astype(np.int32)
+        check_argmax_accept(lg, parent, draft, etok, f"{dtype}/V{V}/s{stride}/n{n}")
+
+
+def test_argmax_accept_random_trees():
+    rng = np.random.default_rng(2024)
+    for case in range(200):
+        n = int(rng.integers(1, 257)) if case % 4 == 0 else int(rng.integers(1, 24))
+        parent = np.array([-1] + [int(rng.integers(-1, i)) for i in range(1, n)], dtype=np.int32)
+        V = int(rng.integers(1, 5)) * 4096 + int(rng.integers(0, 9))
+        x = rng.standard_normal((n, V)).astype(np.float32)
+        bits = bf16_bits_from_f32(x)
+        etok = oracle.argmax_rows(oracle.bf16_bits_to_f64(bits))
+        draft = np.where(rng.random(n) < 0.8, etok, (etok + 1) % V).astype(np.int32)
+        check_argmax_accept(dev_bf16(bits), parent, draft, etok, f"random/{case}")
