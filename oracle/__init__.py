@@ -10,6 +10,7 @@ from .tree_verify import (  # noqa: F401
     anc_bitmask_words,
     argmax_rows,
     bf16_bits_to_f64,
+    kv_commit,
     tree_attention,
     tree_structure,
     validate_parent,

@@ -167,6 +167,28 @@ def accept(parent, draft, tok):
     return len(nodes), nodes, draft[nodes], bonus
 
 
+def kv_commit(k, v, L: int, nodes):
+    """Key/value cache after committing an accepted path.
+
+    The verify rule keeps the drafted tokens the target agreed with and drops the rest
+    (DFlash contributor guide, section "What is DFlash?"); on a tree the kept tokens are
+    the accepted root-to-node path. Their keys and values therefore move to the rows
+    right after the context, in path order: new row ``L + j`` is old row ``L + nodes[j]``
+    for ``j < len(nodes)``; every other row is unchanged (rows past ``L + len(nodes)`` are
+    no longer part of the committed sequence). ``k``, ``v``: arrays ``[T, ...]`` whose rows
+    ``L + i`` hold tree node i; values are copied bit for bit. Returns new arrays.
+    """
+    nodes = np.asarray(nodes, dtype=np.int64)
+    n = k.shape[0] - L
+    if nodes.size and (nodes.min() < 0 or nodes.max() >= n or np.any(np.diff(nodes) <= 0)):
+        raise ValueError("nodes must be increasing tree node indices")
+    k2, v2 = np.array(k, copy=True), np.array(v, copy=True)
+    rows = L + nodes
+    k2[L:L + nodes.size] = k[rows]
+    v2[L:L + nodes.size] = v[rows]
+    return k2, v2
+
+
 def verify(q, k, v, parent, scale, logits, draft):
     """The whole step: attention output, row maxima and the acceptance result."""
     out, lse = tree_attention(q, k, v, parent, scale)
