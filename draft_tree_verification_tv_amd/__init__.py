@@ -15,6 +15,7 @@ from .tv import (  # noqa: F401
     argmax_accept,
     argmax_workspace,
     argmax_workspace_size,
+    kv_commit,
     lib,
     status_string,
     tree_attn,

@@ -131,4 +131,16 @@ int tv_argmax_accept(const void* logits, int dtype, int N, int V, int64_t row_st
                                             static_cast<hipStream_t>(stream)));
 }
 
+int tv_kv_commit(void* k, void* v, int64_t kv_stride_t, int64_t kv_stride_h, int Hkv, int D, int L, int N,
+                 const int32_t* accept_len, const int32_t* accept_nodes, int32_t* new_len, int32_t* dev_error,
+                 void* stream) {
+  if (!k || !v || !accept_len || !accept_nodes) return TV_ERR_INVALID_ARG;
+  if (N < 1 || N > TV_MAX_NODES || L < 0 || Hkv < 1 || D < 8 || D % 8 != 0 || D > 4096) return TV_ERR_INVALID_ARG;
+  if (kv_stride_t < (int64_t)Hkv * D || kv_stride_h < D || kv_stride_t % 8 != 0 || kv_stride_h % 8 != 0)
+    return TV_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v)) return TV_ERR_INVALID_ARG;
+  return status_of(tv::launch_kv_commit(k, v, kv_stride_t, kv_stride_h, Hkv, D, L, N, accept_len, accept_nodes,
+                                        new_len, dev_error, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -162,6 +162,10 @@ hipError_t launch_accept(const int32_t* parent, const int32_t* draft, const int3
                          int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
                          int32_t* bonus, int32_t* dev_error, hipStream_t stream);
 
+hipError_t launch_kv_commit(void* k, void* v, int64_t st, int64_t sh, int Hkv, int D, int L, int N,
+                            const int32_t* accept_len, const int32_t* accept_nodes, int32_t* new_len,
+                            int32_t* dev_error, hipStream_t stream);
+
 struct ArgmaxPlan {
   int chunks;     // workgroups per row
   int chunk_len;  // elements per workgroup (multiple of 8)

@@ -25,7 +25,7 @@ HEAD_DIM = 128
 
 EXPORTS = ("tv_abi_version", "tv_status_string", "tv_validate_tree_host", "tv_tree_prep",
            "tv_tree_attn_workspace_size", "tv_tree_attn", "tv_argmax_workspace_size",
-           "tv_argmax", "tv_accept", "tv_argmax_accept")
+           "tv_argmax", "tv_accept", "tv_argmax_accept", "tv_kv_commit")
 
 
 class TVError(RuntimeError):
@@ -73,6 +73,8 @@ def lib():
         L.tv_argmax_accept.restype = _i32
         L.tv_argmax_accept.argtypes = [_vp, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                        _vp, _vp]
+        L.tv_kv_commit.restype = _i32
+        L.tv_kv_commit.argtypes = [_vp, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
         if L.tv_abi_version() != 1:
             raise RuntimeError("libtv ABI version mismatch")
         _lib = L
@@ -237,6 +239,26 @@ def argmax_accept(logits, parent, draft, tok=None, out=None, workspace=None, V=N
                                   _ptr(ln), _ptr(nodes), _ptr(toks), _ptr(bonus), _ptr(workspace),
                                   workspace.numel(), _ptr(dev_error), _stream(stream)), "tv_argmax_accept")
     return tok, out
+
+
+def kv_commit(k, v, L, accept_len, accept_nodes, N=None, new_len=None, dev_error=None, stream=None):
+    """Move the accepted nodes' K/V rows (cache rows L + node) to rows L + 0, 1, ... in path
+    order, in place. k, v: [>= L+N, Hkv, D] 2-byte tensors sharing strides (last dim
+    contiguous); accept_len, accept_nodes: int32 device tensors as tv_accept writes them."""
+    for name, t in (("k", k), ("v", v)):
+        _need_cuda(name, t)
+        if t.element_size() != 2 or t.dim() != 3:
+            raise ValueError(f"{name} must be a 3-D tensor of 2-byte elements")
+    if k.stride() != v.stride() or k.stride(2) != 1 or k.shape != v.shape:
+        raise ValueError("k and v must share shape and strides with a contiguous last dim")
+    _need_cuda("accept_len", accept_len, torch.int32)
+    _need_cuda("accept_nodes", accept_nodes, torch.int32)
+    N = accept_nodes.numel() if N is None else N
+    if k.shape[0] < L + N:
+        raise ValueError("k/v must hold L + N rows")
+    _check(lib().tv_kv_commit(_ptr(k), _ptr(v), k.stride(0), k.stride(1), k.shape[1], k.shape[2], L, N,
+                              _ptr(accept_len), _ptr(accept_nodes), _ptr(new_len), _ptr(dev_error), _stream(stream)),
+           "tv_kv_commit")
 
 
 def verify(q, k, v, parent, logits, draft, L=None, scale=None, num_splits=0, attn_workspace=None,

@@ -18,6 +18,7 @@
  *   tv_argmax     row argmax of the target logits                      (bit exact)
  *   tv_accept     longest accepted root-to-node path                   (bit exact)
  *   tv_argmax_accept   the two above in one call
+ *   tv_kv_commit  moves the accepted nodes' K/V rows behind the context   (bit exact)
  *
  * Conventions shared by every call
  *   - Pointers are DEVICE pointers unless the name ends in _host. The caller owns every
@@ -158,6 +159,27 @@ int tv_argmax_accept(const void* logits, int dtype, int N, int V, int64_t row_st
                      int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
                      int32_t* bonus, void* workspace, size_t workspace_bytes,
                      int32_t* dev_error, void* stream);
+
+/*
+ * Commit of the accepted path (the step after acceptance). Verification keeps the drafted
+ * tokens the target agreed with and drops the rest (DFlash contributor guide, section
+ * "What is DFlash?"); the kept tokens' keys and values, written at cache rows L + node by
+ * the verify pass, move in place to rows L + 0, 1, ... in path order:
+ *     for j in [0, *accept_len): row L + j <- row L + accept_nodes[j]   (K and V, all heads)
+ * Other rows are not touched; the committed sequence then has length L + *accept_len.
+ *   k, v         the cache of tv_tree_attn (same layout; any 2-byte element type; rows
+ *                [0, L + N) valid); modified in place. 16-byte aligned.
+ *   kv_stride_t, kv_stride_h, Hkv, D   as for tv_tree_attn (D a multiple of 8, <= 4096).
+ *   accept_len, accept_nodes   device int32, as tv_accept writes them.
+ *   new_len      optional int32 [1]: receives L + *accept_len.
+ *   dev_error    optional: receives TV_ERR_INVALID_ARG when *accept_len is outside [0, N]
+ *                or the nodes are not increasing indices with accept_nodes[j] in [j, N);
+ *                the cache is then left unchanged.
+ * Limits: 1 <= N <= TV_MAX_NODES, L >= 0.
+ */
+int tv_kv_commit(void* k, void* v, int64_t kv_stride_t, int64_t kv_stride_h, int Hkv, int D,
+                 int L, int N, const int32_t* accept_len, const int32_t* accept_nodes,
+                 int32_t* new_len, int32_t* dev_error, void* stream);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_documented_calls():
     names = declared_functions()
-    for n in ("tv_tree_attn", "tv_argmax", "tv_accept", "tv_argmax_accept", "tv_tree_prep", "tv_abi_version",
+    for n in ("tv_tree_attn", "tv_argmax", "tv_accept", "tv_argmax_accept", "tv_kv_commit", "tv_tree_prep",
+              "tv_abi_version",
               "tv_validate_tree_host"):
         assert n in names
     assert set(names) == set(tv.EXPORTS)
@@ -145,6 +146,25 @@ def test_argmax_accept_workspace_checks():
     assert L.tv_argmax_accept(*args, None, 1 << 30, None, None) == 4
     assert L.tv_argmax_accept(*args, FAKE, 8, None, None) == 4
     assert L.tv_argmax_accept(*args, ctypes.c_void_p(0x10008), 1 << 30, None, None) == 4
+
+
+# tv_kv_commit(k, v, stride_t, stride_h, Hkv, D, L, N, accept_len, accept_nodes, new_len, dev_error, stream)
+@pytest.mark.parametrize("args,status", [
+    ((None, FAKE, 1024, 128, 8, 128, 100, 16, FAKE, FAKE), 1),
+    ((FAKE, None, 1024, 128, 8, 128, 100, 16, FAKE, FAKE), 1),
+    ((FAKE, FAKE, 1024, 128, 8, 128, 100, 16, None, FAKE), 1),
+    ((FAKE, FAKE, 1024, 128, 8, 128, 100, 16, FAKE, None), 1),
+    ((FAKE, FAKE, 1024, 128, 8, 128, 100, 0, FAKE, FAKE), 1),
+    ((FAKE, FAKE, 1024, 128, 8, 128, 100, 257, FAKE, FAKE), 1),
+    ((FAKE, FAKE, 1024, 128, 8, 128, -1, 16, FAKE, FAKE), 1),
+    ((FAKE, FAKE, 1024, 128, 0, 128, 100, 16, FAKE, FAKE), 1),
+    ((FAKE, FAKE, 1024, 128, 8, 12, 100, 16, FAKE, FAKE), 1),
+    ((FAKE, FAKE, 1020, 128, 8, 128, 100, 16, FAKE, FAKE), 1),
+    ((FAKE, FAKE, 1024, 124, 8, 128, 100, 16, FAKE, FAKE), 1),
+    ((ctypes.c_void_p(0x10008), FAKE, 1024, 128, 8, 128, 100, 16, FAKE, FAKE), 1),
+])
+def test_kv_commit_rejects(args, status):
+    assert tv.lib().tv_kv_commit(*args, None, None, None) == status
 
 
 def test_tree_prep_rejects():

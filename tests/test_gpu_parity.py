@@ -396,3 +396,88 @@ def test_argmax_accept_random_trees():
         etok = oracle.argmax_rows(oracle.bf16_bits_to_f64(bits))
         draft = np.where(rng.random(n) < 0.8, etok, (etok + 1) % V).astype(np.int32)
         check_argmax_accept(dev_bf16(bits), parent, draft, etok, f"random/{case}")
+
+
+# ------------------------------------------------------ NEXT: accepted-path KV commit
+
+
+def _commit_case(rng, n, L, hkv, d, stride_extra_heads=0, chain=False):
+    if chain:   # long accepted paths (several batches of 16 rows)
+        parent = np.arange(-1, n - 1, dtype=np.int32)
+    else:
+        parent = np.array([-1] + [int(rng.integers(-1, i)) for i in range(1, n)], dtype=np.int32)
+    tok = rng.integers(0, 3, n).astype(np.int32)
+    draft = np.where(rng.random(n) < (0.98 if chain else 0.8), tok, (tok + 1) % 3).astype(np.int32)
+    hs = hkv + stride_extra_heads
+    k = rng.integers(0, 1 << 16, (L + n + 3, hs, d), dtype=np.uint16)
+    v = rng.integers(0, 1 << 16, (L + n + 3, hs, d), dtype=np.uint16)
+    return parent, draft, tok, k, v
+
+
+def _run_commit(parent, draft, tok, k, v, L, hkv):
+    """GPU accept feeding the GPU commit; compared bit for bit with the oracle."""
+    kd = torch.from_numpy(k.view(np.int16)).cuda()
+    vd = torch.from_numpy(v.view(np.int16)).cuda()
+    kv_k, kv_v = kd[:, :hkv], vd[:, :hkv]
+    ln, nodes, _, _ = tv.accept(dev_i32(parent), dev_i32(draft), dev_i32(tok))
+    new_len = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tv.kv_commit(kv_k, kv_v, L, ln, nodes, new_len=new_len, dev_error=err)
+    torch.cuda.synchronize()
+    m, enodes, _, _ = oracle.accept(parent, draft, tok)
+    ek, ev = oracle.kv_commit(k[:, :hkv], v[:, :hkv], L, enodes)
+    gk = kd.cpu().numpy().view(np.uint16)
+    gv = vd.cpu().numpy().view(np.uint16)
+    assert err.item() == 0 and new_len.item() == L + m
+    assert np.array_equal(gk[:, :hkv], ek) and np.array_equal(gv[:, :hkv], ev)
+    assert np.array_equal(gk[:, hkv:], k[:, hkv:]) and np.array_equal(gv[:, hkv:], v[:, hkv:])
+    return m
+
+
+def test_kv_commit_random_trees():
+    rng = np.random.default_rng(77)
+    lens = []
+    for case in range(60):
+        n = int(rng.integers(1, 257)) if case % 5 == 0 else int(rng.integers(1, 40))
+        L = int(rng.integers(0, 300))
+        hkv, d = [(8, 128), (2, 128), (1, 64), (4, 8)][case % 4]
+        chain = case % 3 == 1
+        parent, draft, tok, k, v = _commit_case(rng, n, L, hkv, d, chain=chain)
+        note(f"kv_commit case {case}: n={n} L={L} hkv={hkv} d={d} chain={chain}")
+        lens.append(_run_commit(parent, draft, tok, k, v, L, hkv))
+    assert max(lens) > 16                           # several batches of 16 rows crossed
+
+
+def test_kv_commit_strided_view_and_chain():
+    rng = np.random.default_rng(3)
+    parent, draft, tok, k, v = _commit_case(rng, 40, 100, 4, 128, stride_extra_heads=3)
+    _run_commit(parent, draft, tok, k, v, 100, 4)
+    n = 20
+    parent = np.arange(-1, n - 1, dtype=np.int32)      # a chain fully accepted: identity
+    k = rng.integers(0, 1 << 16, (50 + n, 2, 128), dtype=np.uint16)
+    v = rng.integers(0, 1 << 16, (50 + n, 2, 128), dtype=np.uint16)
+    assert _run_commit(parent, np.zeros(n, np.int32), np.zeros(n, np.int32), k, v, 50, 2) == n
+    # nothing accepted: the cache must not change
+    assert _run_commit(parent, np.zeros(n, np.int32), np.ones(n, np.int32), k, v, 50, 2) == 0
+
+
+def test_kv_commit_full_size_cache():
+    w = make("long_128k", 0, parts=("tree", "qkv"))
+    tok = np.where(w.matched, w.draft, (w.draft + 1) % w.V).astype(np.int32)
+    note(f"kv_commit long_128k planted length {w.planted_len}")
+    m = _run_commit(w.parent, w.draft, tok, w.k, w.v, w.L, w.Hkv)
+    assert m == w.planted_len
+
+
+def test_kv_commit_rejects_bad_paths_on_device():
+    rng = np.random.default_rng(9)
+    k = rng.integers(0, 1 << 16, (60, 2, 128), dtype=np.uint16)
+    kd = torch.from_numpy(k.view(np.int16)).cuda()
+    vd = kd.clone()
+    for ln, nodes in ((3, [0, 2, 2, 9]), (2, [1, 0, 5, 6]), (5, [0, 1, 2, 3]), (-1, [0, 1, 2, 3]),
+                      (2, [0, 4, 0, 0])):
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        tv.kv_commit(kd, vd, 50, dev_i32([ln]), dev_i32(nodes), dev_error=err)
+        torch.cuda.synchronize()
+        assert err.item() == 1, (ln, nodes)
+        assert np.array_equal(kd.cpu().numpy().view(np.uint16), k)
