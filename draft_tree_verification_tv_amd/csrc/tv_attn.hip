@@ -488,12 +488,12 @@ AttnPlan attn_plan(int N, int L, int Hq, int Hkv, int num_splits, int num_cus) {
   const int tiles = (p.T + KT - 1) / KT;
   int S = num_splits;
   if (S <= 0) {
-    // One workgroup per CU (the four LDS stages and the tree masks take 138 KB); at least 8 tiles per split
-    // so that partial-output traffic stays small against the KV stream.
+    // One workgroup per CU (the four LDS stages and the tree masks take 138 KB): enough
+    // splits to give every CU a workgroup, down to one 64-key tile per split. Short
+    // sequences are latency-bound, so filling the chip beats saving partial-output
+    // traffic; long ones get long splits anyway.
     const int units = Hkv * p.RT;
     S = (num_cus + units - 1) / units;
-    const int cap = tiles / 8 > 0 ? tiles / 8 : 1;
-    if (S > cap) S = cap;
   }
   if (S > tiles) S = tiles;
   if (S < 1) S = 1;
