@@ -118,15 +118,16 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
+        # Kernels go to the current stream: `stream` when eager, the capture stream while a
+        # graph is being recorded.
         if ev:
             ev[0].record(stream)
         for b in range(layers):
-            tv.tree_attn(q, K[b], Vc[b], parent, L=L, scale=w.scale, num_splits=args.splits, out=out, workspace=ws,
-                         stream=stream)
+            tv.tree_attn(q, K[b], Vc[b], parent, L=L, scale=w.scale, num_splits=args.splits, out=out, workspace=ws)
         if ev:
             ev[1].record(stream)
         # argmax over the vocabulary and the accept walk: one call, two launches
-        tv.argmax_accept(logits, parent, draft, tok=tok, out=acc, workspace=am_ws, stream=stream)
+        tv.argmax_accept(logits, parent, draft, tok=tok, out=acc, workspace=am_ws)
         if ev:
             ev[2].record(stream)
 
@@ -154,6 +155,22 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # The same step captured once as a HIP graph and replayed (every call only enqueues
+    # kernels on the stream, so the whole step is capturable).
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms_per_step = g0.elapsed_time(g1) / args.steps
+    del graph
+
     attn_ms = np.array([e[0].elapsed_time(e[1]) for e in events]) / layers
     tokens_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
     t_attn_us = float(np.median(attn_ms) * 1e3)
@@ -167,7 +184,7 @@ def main():
     achieved = algo_bytes / (t_attn_us * 1e-6) / 1e9
     kv_gbps = kv_bytes / (t_attn_us * 1e-6) / 1e9
     log(f"attn {t_attn_us:.1f} us/call ({kv_gbps:.0f} GB/s KV, {kv_gbps / HBM_PEAK_GBS:.1%} of peak), "
-        f"argmax+accept {t_tokens_us:.1f} us, step {ms_per_step:.2f} ms")
+        f"argmax+accept {t_tokens_us:.1f} us, step {ms_per_step:.2f} ms (graph replay {graph_ms_per_step:.2f} ms)")
 
     parity = None
     if not args.no_check:
@@ -246,6 +263,7 @@ def main():
         "breakdown_us": {"attn_per_call": round(t_attn_us, 2), "argmax_accept": round(t_tokens_us, 2),
                          "attn_p10": round(float(np.percentile(attn_ms, 10) * 1e3), 2),
                          "attn_p90": round(float(np.percentile(attn_ms, 90) * 1e3), 2)},
+        "graph_ms_per_step": round(graph_ms_per_step, 3),
         "kv_gbps": round(kv_gbps, 1),
         "kv_hbm_frac": round(kv_gbps / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
