@@ -5,6 +5,7 @@ the smoke check and the benchmark's CPU-baseline leg may import it; the HIP libr
 its binding never do, and this package imports nothing from them.
 """
 
+from .sampling import philox4x32_10, sample_accept, sample_rows, uniforms  # noqa: F401
 from .tree_verify import (  # noqa: F401
     accept,
     anc_bitmask_words,
