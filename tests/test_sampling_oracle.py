@@ -29,6 +29,7 @@ def test_philox_known_answers(ctr, key, expect):
 def test_uniforms_in_open_interval_and_uniform():
     u = oracle.uniforms(4, 50000, seed=1234, offset=7)
     assert u.min() > 0 and u.max() < 1
+    assert np.array_equal(u.astype(np.float32).astype(np.float64), u)   # exact in float32
     hist, _ = np.histogram(u.ravel(), bins=20, range=(0, 1))
     expected = u.size / 20
     chi2 = ((hist - expected) ** 2 / expected).sum()
