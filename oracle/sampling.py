@@ -12,8 +12,9 @@ for the same (seed, counter). Drafts are then accepted exactly as in greedy veri
 
 Counter layout: key = (seed low 32 bits, seed high 32 bits); counter = (v // 4, node,
 offset low 32 bits, offset high 32 bits); word v % 4 of the output gives the uniform for
-vocabulary index v from its top 24 bits: u = ((word >> 8) + 0.5) / 2^24, strictly inside
-(0, 1) and exactly representable in float32, so every implementation draws the same u.
+vocabulary index v from its top 23 bits: u = ((word >> 9) + 0.5) / 2^23, strictly inside
+(0, 1) and exactly representable in float32 (at most 24 significant bits), so every
+implementation draws the same u.
 """
 
 from __future__ import annotations
@@ -60,7 +61,7 @@ def uniforms(n_nodes: int, V: int, seed: int, offset: int) -> np.ndarray:
         words = philox4x32_10((v // np.uint64(4), np.uint64(i), np.uint64(offset & MASK32),
                                np.uint64((offset >> 32) & MASK32)), key)
         w = np.choose((v % np.uint64(4)).astype(np.int64), words)
-        out[i] = ((w >> np.uint64(8)).astype(np.float64) + 0.5) / 16777216.0
+        out[i] = ((w >> np.uint64(9)).astype(np.float64) + 0.5) / 8388608.0
     return out
 
 
