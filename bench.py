@@ -171,6 +171,25 @@ def main():
     graph_ms_per_step = g0.elapsed_time(g1) / args.steps
     del graph
 
+    # Next-row calls on the same inputs, timed alone (not part of `value`): sampled
+    # verification at temperature 1 and the KV commit of the accepted path (on layer 1's
+    # cache, whose values do not matter for the timing).
+    def timed(fn, reps=20):
+        fn()
+        torch.cuda.synchronize()
+        t0e, t1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0e.record(stream)
+        for _ in range(reps):
+            fn()
+        t1e.record(stream)
+        torch.cuda.synchronize()
+        return t0e.elapsed_time(t1e) * 1e3 / reps
+
+    sample_us = timed(lambda: tv.sample_accept(logits, parent, draft, 1.0, 1234, 0, tok=tok, out=acc,
+                                               workspace=am_ws))
+    tv.argmax_accept(logits, parent, draft, tok=tok, out=acc, workspace=am_ws)
+    commit_us = timed(lambda: tv.kv_commit(K[1], Vc[1], L, acc[0], acc[1]))
+
     attn_ms = np.array([e[0].elapsed_time(e[1]) for e in events]) / layers
     tokens_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
     t_attn_us = float(np.median(attn_ms) * 1e3)
@@ -264,6 +283,7 @@ def main():
                          "attn_p10": round(float(np.percentile(attn_ms, 10) * 1e3), 2),
                          "attn_p90": round(float(np.percentile(attn_ms, 90) * 1e3), 2)},
         "graph_ms_per_step": round(graph_ms_per_step, 3),
+        "next_rows_us": {"sample_accept_T1": round(sample_us, 2), "kv_commit": round(commit_us, 2)},
         "kv_gbps": round(kv_gbps, 1),
         "kv_hbm_frac": round(kv_gbps / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -17,6 +17,7 @@ from .tv import (  # noqa: F401
     argmax_workspace_size,
     kv_commit,
     lib,
+    sample_accept,
     status_string,
     tree_attn,
     tree_attn_workspace_size,

@@ -143,4 +143,21 @@ int tv_kv_commit(void* k, void* v, int64_t kv_stride_t, int64_t kv_stride_h, int
                                         new_len, dev_error, static_cast<hipStream_t>(stream)));
 }
 
+int tv_sample_accept(const void* logits, int dtype, int N, int V, int64_t row_stride, float temperature,
+                     uint64_t seed, uint64_t offset, const int32_t* parent, const int32_t* draft, int32_t* tok,
+                     int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens, int32_t* bonus,
+                     void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream) {
+  if (!logits || !tok || !parent || !draft || !accept_len || !accept_nodes || !accept_tokens)
+    return TV_ERR_INVALID_ARG;
+  if (N < 1 || N > TV_MAX_NODES || V < 1 || V >= INT32_MAX - 8 || row_stride < V) return TV_ERR_INVALID_ARG;
+  if (dtype != TV_BF16 && dtype != TV_F32) return TV_ERR_INVALID_ARG;
+  if (!(temperature > 0.f) || !std::isfinite(temperature) || !std::isfinite(1.0f / temperature))
+    return TV_ERR_INVALID_ARG;
+  const size_t need = tv::argmax_workspace_bytes(N, V);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return TV_ERR_WORKSPACE;
+  return status_of(tv::launch_sample_accept(logits, dtype, N, V, row_stride, temperature, seed, offset, parent,
+                                            draft, tok, accept_len, accept_nodes, accept_tokens, bonus, workspace,
+                                            dev_error, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -179,6 +179,116 @@ __global__ __launch_bounds__(256) void argmax_final(int N, int chunks, const flo
   if (lane == 0) tok[row] = r.i == INT_MAX ? -1 : r.i;
 }
 
+// ---- sampled targets (temperature > 0)
+//
+// The target's token for node i is a sample from softmax(logits[i] / T), drawn as the
+// lowest index of the largest logit / T + G with Gumbel noise G = -ln(-ln u). The uniforms
+// come from Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
+// as 1, 2, 3", SC 2011): key (seed lo, seed hi), counter (v / 4, node, offset lo, offset
+// hi); word v % 4 gives u = ((word >> 9) + 0.5) / 2^23, exact in float32.
+
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                               uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+struct SampleKey {
+  uint32_t k0, k1, o0, o1;  // seed and offset halves
+  float inv_t;              // 1 / temperature
+};
+
+__device__ __forceinline__ float gumbel_score(float x, uint32_t word, float inv_t) {
+  const float u = ((float)(word >> 9) + 0.5f) * 0x1p-23f;
+  return __builtin_fmaf(x, inv_t, -__logf(-__logf(u)));
+}
+
+// Grid (slices, rows), 256 threads; the slice layout and outputs are those of
+// argmax_partial. Each thread scores eight consecutive entries per step (two Philox
+// blocks); a row that is not 16-byte aligned is read element by element.
+template <bool kF32, bool kVec>
+__global__ __launch_bounds__(kBlock) void sample_partial(const char* __restrict__ logits, int V, int64_t row_bytes,
+                                                         int chunks, int chunk_len, SampleKey key,
+                                                         int32_t* __restrict__ tok, float* __restrict__ part_v,
+                                                         int* __restrict__ part_i) {
+  constexpr int ESZ = kF32 ? 4 : 2;
+  const int row = blockIdx.y;
+  const int c = blockIdx.x;
+  const char* rp = logits + (int64_t)row * row_bytes;
+  const int begin = c * chunk_len;
+  const int end = min(V, begin + chunk_len);
+  const int tid = threadIdx.x;
+  Best b{-INFINITY, INT_MAX};
+  // Entries [e, e + 8): e is a multiple of 8 relative to the row, so the two Philox blocks
+  // are (e / 4) and (e / 4 + 1).
+  for (int e = begin + tid * 8; e < end; e += kBlock * 8) {
+    float x[8];
+    if (kVec && e + 8 <= end) {
+      if constexpr (kF32) {
+        const u32x4 w0 = *reinterpret_cast<const u32x4*>(rp + (int64_t)e * ESZ);
+        const u32x4 w1 = *reinterpret_cast<const u32x4*>(rp + (int64_t)e * ESZ + 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[j] = __uint_as_float(w0[j]);
+          x[4 + j] = __uint_as_float(w1[j]);
+        }
+      } else {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(rp + (int64_t)e * ESZ);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[2 * j] = bf16_lo(w[j]);
+          x[2 * j + 1] = bf16_hi(w[j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = (e + j < end) ? load_one<kF32>(rp, e + j) : -INFINITY;
+    }
+    const u32x4 r0 = philox4x32_10((uint32_t)(e >> 2), (uint32_t)row, key.o0, key.o1, key.k0, key.k1);
+    const u32x4 r1 = philox4x32_10((uint32_t)(e >> 2) + 1u, (uint32_t)row, key.o0, key.o1, key.k0, key.k1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (e + j < end) {
+        const float sc = gumbel_score(x[j], j < 4 ? r0[j] : r1[j - 4], key.inv_t);
+        if (sc > b.v || b.i == INT_MAX) {
+          b.v = sc;
+          b.i = e + j;
+        }
+      }
+    }
+  }
+
+  __shared__ float sv[kBlock / 64];
+  __shared__ int si[kBlock / 64];
+  b = wave_reduce(b);
+  const int wave = tid >> 6;
+  if ((tid & 63) == 0) {
+    sv[wave] = b.v;
+    si[wave] = b.i;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    Best r{sv[0], si[0]};
+    for (int w = 1; w < kBlock / 64; ++w) r = better(r, Best{sv[w], si[w]});
+    if (chunks == 1) {
+      tok[row] = r.i == INT_MAX ? -1 : r.i;
+    } else {
+      part_v[(int64_t)row * chunks + c] = r.v;
+      part_i[(int64_t)row * chunks + c] = r.i;
+    }
+  }
+}
+
 // One workgroup finishes the verify step: thread i reduces node row i's slice results to
 // the row argmax (loads batched eight slices at a time, indices clamped so that no load is
 // conditional; a repeated (value, index) pair cannot change the result), keeps the tokens
@@ -309,6 +419,48 @@ hipError_t launch_argmax_accept(const void* logits, int dtype, int N, int V, int
   float* part_v = reinterpret_cast<float*>(ws);
   int* part_i = reinterpret_cast<int*>(ws + (parts * sizeof(float) + 255) / 256 * 256);
   hipError_t e = launch_argmax_partial(logits, dtype, N, V, row_bytes, vec, p, tok, part_v, part_i, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(argmax_accept_kernel, dim3(1), dim3(kFuseThreads), 0, stream, N, p.chunks, part_v, part_i,
+                     tok, parent, draft, accept_len, accept_nodes, accept_tokens, bonus, dev_error);
+  return hipGetLastError();
+}
+
+}  // namespace tv
+
+namespace tv {
+
+hipError_t launch_sample_accept(const void* logits, int dtype, int N, int V, int64_t row_stride, float temperature,
+                                uint64_t seed, uint64_t offset, const int32_t* parent, const int32_t* draft,
+                                int32_t* tok, int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
+                                int32_t* bonus, void* workspace, int32_t* dev_error, hipStream_t stream) {
+  const int esize = dtype == TV_F32 ? 4 : 2;
+  const int64_t row_bytes = row_stride * esize;
+  const bool vec = ((uintptr_t)logits % 16 == 0) && (row_bytes % 16 == 0);
+  const ArgmaxPlan p = argmax_plan(N, V, dtype, vec);
+  const size_t parts = (size_t)N * argmax_plan(N, V, TV_F32, false).chunks;
+  char* ws = static_cast<char*>(workspace);
+  float* part_v = reinterpret_cast<float*>(ws);
+  int* part_i = reinterpret_cast<int*>(ws + (parts * sizeof(float) + 255) / 256 * 256);
+  SampleKey key{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)offset, (uint32_t)(offset >> 32),
+                1.0f / temperature};
+  const dim3 grid(p.chunks, N);
+  const char* lg = static_cast<const char*>(logits);
+  if (dtype == TV_F32) {
+    if (vec)
+      hipLaunchKernelGGL((sample_partial<true, true>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes, p.chunks,
+                         p.chunk_len, key, tok, part_v, part_i);
+    else
+      hipLaunchKernelGGL((sample_partial<true, false>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes, p.chunks,
+                         p.chunk_len, key, tok, part_v, part_i);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((sample_partial<false, true>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes, p.chunks,
+                         p.chunk_len, key, tok, part_v, part_i);
+    else
+      hipLaunchKernelGGL((sample_partial<false, false>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes, p.chunks,
+                         p.chunk_len, key, tok, part_v, part_i);
+  }
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(argmax_accept_kernel, dim3(1), dim3(kFuseThreads), 0, stream, N, p.chunks, part_v, part_i,
                      tok, parent, draft, accept_len, accept_nodes, accept_tokens, bonus, dev_error);

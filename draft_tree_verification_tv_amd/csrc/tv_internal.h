@@ -162,6 +162,10 @@ hipError_t launch_accept(const int32_t* parent, const int32_t* draft, const int3
                          int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
                          int32_t* bonus, int32_t* dev_error, hipStream_t stream);
 
+hipError_t launch_sample_accept(const void* logits, int dtype, int N, int V, int64_t row_stride, float temperature,
+                                uint64_t seed, uint64_t offset, const int32_t* parent, const int32_t* draft,
+                                int32_t* tok, int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
+                                int32_t* bonus, void* workspace, int32_t* dev_error, hipStream_t stream);
 hipError_t launch_kv_commit(void* k, void* v, int64_t st, int64_t sh, int Hkv, int D, int L, int N,
                             const int32_t* accept_len, const int32_t* accept_nodes, int32_t* new_len,
                             int32_t* dev_error, hipStream_t stream);

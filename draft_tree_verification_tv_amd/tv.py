@@ -25,7 +25,7 @@ HEAD_DIM = 128
 
 EXPORTS = ("tv_abi_version", "tv_status_string", "tv_validate_tree_host", "tv_tree_prep",
            "tv_tree_attn_workspace_size", "tv_tree_attn", "tv_argmax_workspace_size",
-           "tv_argmax", "tv_accept", "tv_argmax_accept", "tv_kv_commit")
+           "tv_argmax", "tv_accept", "tv_argmax_accept", "tv_sample_accept", "tv_kv_commit")
 
 
 class TVError(RuntimeError):
@@ -73,6 +73,9 @@ def lib():
         L.tv_argmax_accept.restype = _i32
         L.tv_argmax_accept.argtypes = [_vp, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                        _vp, _vp]
+        L.tv_sample_accept.restype = _i32
+        L.tv_sample_accept.argtypes = [_vp, _i32, _i32, _i32, _i64, _f32, ctypes.c_uint64, ctypes.c_uint64, _vp, _vp,
+                                       _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]
         L.tv_kv_commit.restype = _i32
         L.tv_kv_commit.argtypes = [_vp, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
         if L.tv_abi_version() != 1:
@@ -238,6 +241,39 @@ def argmax_accept(logits, parent, draft, tok=None, out=None, workspace=None, V=N
     _check(lib().tv_argmax_accept(_ptr(logits), dt, N, V, logits.stride(0), _ptr(parent), _ptr(draft), _ptr(tok),
                                   _ptr(ln), _ptr(nodes), _ptr(toks), _ptr(bonus), _ptr(workspace),
                                   workspace.numel(), _ptr(dev_error), _stream(stream)), "tv_argmax_accept")
+    return tok, out
+
+
+def sample_accept(logits, parent, draft, temperature, seed, offset=0, tok=None, out=None, workspace=None, V=None,
+                  dev_error=None, stream=None):
+    """Sampled verification at temperature > 0: tok[i] is a sample from softmax(logits[i] / T)
+    (Gumbel-max over Philox-4x32-10 keyed by seed, counter offset), then the longest
+    accepted path. Returns (tok [N], (accept_len [1], nodes [N], tokens [N], bonus [1]))."""
+    _need_cuda("logits", logits)
+    for name, t in (("parent", parent), ("draft", draft)):
+        _need_cuda(name, t, torch.int32)
+    if logits.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("logits must be bf16 or fp32")
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be 2-D with a contiguous last dim")
+    N = logits.shape[0]
+    if parent.numel() != N or draft.numel() != N:
+        raise ValueError("parent and draft must have one entry per logits row")
+    V = logits.shape[1] if V is None else V
+    dev = logits.device
+    if tok is None:
+        tok = torch.empty(N, dtype=torch.int32, device=dev)
+    if out is None:
+        out = (torch.empty(1, dtype=torch.int32, device=dev), torch.empty(N, dtype=torch.int32, device=dev),
+               torch.empty(N, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev))
+    if workspace is None:
+        workspace = argmax_workspace(N, V, dev)
+    ln, nodes, toks, bonus = out
+    dt = TV_F32 if logits.dtype == torch.float32 else TV_BF16
+    _check(lib().tv_sample_accept(_ptr(logits), dt, N, V, logits.stride(0), float(temperature), int(seed), int(offset),
+                                  _ptr(parent), _ptr(draft), _ptr(tok), _ptr(ln), _ptr(nodes), _ptr(toks),
+                                  _ptr(bonus), _ptr(workspace), workspace.numel(), _ptr(dev_error), _stream(stream)),
+           "tv_sample_accept")
     return tok, out
 
 

@@ -18,6 +18,7 @@
  *   tv_argmax     row argmax of the target logits                      (bit exact)
  *   tv_accept     longest accepted root-to-node path                   (bit exact)
  *   tv_argmax_accept   the two above in one call
+ *   tv_sample_accept   the same with sampled targets (temperature > 0)
  *   tv_kv_commit  moves the accepted nodes' K/V rows behind the context   (bit exact)
  *
  * Conventions shared by every call
@@ -159,6 +160,24 @@ int tv_argmax_accept(const void* logits, int dtype, int N, int V, int64_t row_st
                      int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
                      int32_t* bonus, void* workspace, size_t workspace_bytes,
                      int32_t* dev_error, void* stream);
+
+/*
+ * Sampled verification (temperature > 0). The pages' sampling call takes a temperature,
+ * 0 meaning the argmax (DFlash contributor guide, section "Coding conventions"); here the
+ * target's token for node i is a sample from softmax(logits[i] / T):
+ *     tok[i] = lowest index of the largest  logits[i][v] / T - ln(-ln u(i, v))
+ * (Gumbel-max). u(i, v) comes from Philox-4x32-10 (Salmon et al., SC 2011) with key
+ * (seed low, seed high) and counter (v / 4, i, offset low, offset high): word v % 4 of the
+ * output gives u = ((word >> 9) + 0.5) / 2^23. The same (seed, offset) repeats the draw;
+ * advance offset between steps. Acceptance then follows tv_accept on these tokens.
+ *   temperature  > 0, finite, with 1/T finite.
+ *   Other arguments and limits as for tv_argmax_accept (same workspace size).
+ */
+int tv_sample_accept(const void* logits, int dtype, int N, int V, int64_t row_stride,
+                     float temperature, uint64_t seed, uint64_t offset, const int32_t* parent,
+                     const int32_t* draft, int32_t* tok, int32_t* accept_len,
+                     int32_t* accept_nodes, int32_t* accept_tokens, int32_t* bonus,
+                     void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream);
 
 /*
  * Commit of the accepted path (the step after acceptance). Verification keeps the drafted

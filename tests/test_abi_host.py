@@ -28,9 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_documented_calls():
     names = declared_functions()
-    for n in ("tv_tree_attn", "tv_argmax", "tv_accept", "tv_argmax_accept", "tv_kv_commit", "tv_tree_prep",
-              "tv_abi_version",
-              "tv_validate_tree_host"):
+    for n in ("tv_tree_attn", "tv_argmax", "tv_accept", "tv_argmax_accept", "tv_sample_accept", "tv_kv_commit",
+              "tv_tree_prep", "tv_abi_version", "tv_validate_tree_host"):
         assert n in names
     assert set(names) == set(tv.EXPORTS)
 
@@ -165,6 +164,28 @@ def test_argmax_accept_workspace_checks():
 ])
 def test_kv_commit_rejects(args, status):
     assert tv.lib().tv_kv_commit(*args, None, None, None) == status
+
+
+@pytest.mark.parametrize("temp", [0.0, -1.0, float("inf"), float("nan"), 1e-45])
+def test_sample_accept_rejects_bad_temperature(temp):
+    L = tv.lib()
+    assert L.tv_sample_accept(FAKE, 0, 4, 100, 100, temp, 1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                              1 << 30, None, None) == 1
+
+
+def test_sample_accept_rejects_args():
+    L = tv.lib()
+    ok = [FAKE, 0, 4, 100, 100, 1.0, 1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None, None]
+    for i in (0, 8, 9, 10, 11, 12, 13):
+        bad = list(ok)
+        bad[i] = None
+        assert L.tv_sample_accept(*bad) == 1, i
+    bad = list(ok)
+    bad[2] = 257
+    assert L.tv_sample_accept(*bad) == 1
+    bad = list(ok)
+    bad[16] = 8
+    assert L.tv_sample_accept(*bad) == 4
 
 
 def test_tree_prep_rejects():

@@ -481,3 +481,90 @@ def test_kv_commit_rejects_bad_paths_on_device():
         torch.cuda.synchronize()
         assert err.item() == 1, (ln, nodes)
         assert np.array_equal(kd.cpu().numpy().view(np.uint16), k)
+
+
+# ------------------------------------------------------ NEXT: sampled verification (T > 0)
+
+
+def _sample_dev(logits_dev, parent, draft, T, seed, offset):
+    tok, (ln, nodes, toks, bonus) = tv.sample_accept(logits_dev, dev_i32(parent), dev_i32(draft), T, seed, offset)
+    torch.cuda.synchronize()
+    return tok.cpu().numpy(), ln.item(), nodes.cpu().numpy(), toks.cpu().numpy(), bonus.item()
+
+
+@pytest.mark.parametrize("name,T,seed,offset", [("tiny_chain", 1.0, 7, 0), ("tiny_chain", 0.3, 7, 1),
+                                                ("budget22", 1.0, 123456789012, 5), ("budget22", 2.5, 3, 1 << 40),
+                                                ("decode_1node", 0.8, 42, 9)])
+def test_sample_accept_matches_oracle(name, T, seed, offset):
+    """Same Philox stream and Gumbel-max rule: the sampled tokens equal the oracle's
+    (a different choice would need the top two scores of a row within float32 rounding),
+    and the walk on them is bit exact."""
+    w = make(name, 0, parts=("tree", "logits"))
+    note(f"sample_accept {name} T={T}")
+    if w.logits_dtype == "bf16":
+        lg, x = dev_bf16(w.logits), oracle.bf16_bits_to_f64(w.logits)
+    else:
+        lg, x = torch.from_numpy(w.logits).cuda(), w.logits.astype(np.float64)
+    etok, (eln, enodes, etoks, ebonus) = oracle.sample_accept(w.parent, w.draft, x, T, seed, offset)
+    tok, ln, nodes, toks, bonus = _sample_dev(lg, w.parent, w.draft, T, seed, offset)
+    assert np.array_equal(tok, etok)
+    assert ln == eln and nodes[:ln].tolist() == enodes.tolist() and toks[:ln].tolist() == etoks.tolist()
+    assert (nodes[ln:] == -1).all() and bonus == ebonus
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V,stride", [(5, 5), (4096, 4096), (8200, 8203), (40000, 40000)])
+def test_sample_accept_layouts(dtype, V, stride):
+    rng = np.random.default_rng(V + stride)
+    n = 19
+    parent = np.array([-1] + [int(rng.integers(-1, i)) for i in range(1, n)], dtype=np.int32)
+    x = (rng.standard_normal((n, stride)) * 2).astype(np.float32)
+    if dtype == "bf16":
+        bits = bf16_bits_from_f32(x)
+        lg, xv = dev_bf16(bits)[:, :V], oracle.bf16_bits_to_f64(bits[:, :V])
+    else:
+        lg, xv = torch.from_numpy(x).cuda()[:, :V], x[:, :V].astype(np.float64)
+    etok = oracle.sample_rows(xv, 1.3, 77, 3)
+    draft = np.where(rng.random(n) < 0.6, etok, (etok + 1) % V).astype(np.int32)
+    tok, ln, nodes, _, bonus = _sample_dev(lg, parent, draft, 1.3, 77, 3)
+    assert np.array_equal(tok, etok)
+    e_ln, e_nodes, _, e_bonus = oracle.accept(parent, draft, etok)
+    assert ln == e_ln and nodes[:ln].tolist() == e_nodes.tolist() and bonus == e_bonus
+
+
+def test_sample_frequencies_follow_softmax():
+    """GPU samples over many offsets: chi-square against softmax(logits / T)."""
+    logits = np.array([0.0, 1.0, -0.5, 2.0, 0.3, -2.0, 1.5, 0.0], dtype=np.float32)
+    T, n = 0.8, 64
+    x = np.tile(logits, (n, 1))
+    lg = torch.from_numpy(x).cuda()
+    parent = np.arange(-1, n - 1, dtype=np.int32)
+    counts = np.zeros(8)
+    for off in range(300):
+        tok, *_ = _sample_dev(lg, parent, np.zeros(n, np.int32), T, 2024, off)
+        counts += np.bincount(tok, minlength=8)
+    p = np.exp(logits / T - (logits / T).max())
+    p /= p.sum()
+    tot = counts.sum()
+    chi2 = ((counts - tot * p) ** 2 / (tot * p)).sum()
+    assert chi2 < 24, (counts, tot * p)          # 7 dof: p ~ 0.001
+
+
+def test_sample_low_temperature_is_greedy_and_repeatable():
+    w = make("branch_8k", 3, parts=("tree", "logits"))
+    lg = dev_bf16(w.logits)
+    tok_g, (ln_g, nodes_g, _, _) = tv.argmax_accept(lg, dev_i32(w.parent), dev_i32(w.draft))
+    tok_s, ln_s, nodes_s, _, _ = _sample_dev(lg, w.parent, w.draft, 1e-6, 5, 0)
+    # At T = 1e-6 one bf16 step of a logit outweighs any Gumbel difference, so the sample is
+    # a maximal logit: the argmax where the maximum is unique, one of the tied maxima else.
+    x = oracle.bf16_bits_to_f64(w.logits)
+    for i in range(w.N):
+        top = np.flatnonzero(x[i] == x[i].max())
+        assert tok_s[i] in top, i
+        if top.size == 1:
+            assert tok_s[i] == tok_g[i].item(), i
+    assert ln_s == ln_g.item() == w.planted_len      # planted rows have a unique +16 maximum
+    a = _sample_dev(lg, w.parent, w.draft, 1.0, 5, 0)[0]
+    b = _sample_dev(lg, w.parent, w.draft, 1.0, 5, 0)[0]
+    c = _sample_dev(lg, w.parent, w.draft, 1.0, 5, 1)[0]
+    assert np.array_equal(a, b) and not np.array_equal(a, c)
