@@ -5,6 +5,13 @@ the smoke check and the benchmark's CPU-baseline leg may import it; the HIP libr
 its binding never do, and this package imports nothing from them.
 """
 
+from .kvquant import (  # noqa: F401
+    dequantize_kv,
+    e4m3_decode,
+    e4m3_encode,
+    quantize_kv,
+    row_scale_exponent,
+)
 from .sampling import philox4x32_10, sample_accept, sample_rows, uniforms  # noqa: F401
 from .tree_verify import (  # noqa: F401
     accept,

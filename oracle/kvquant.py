@@ -1,0 +1,93 @@
+"""Quantised key/value cache for the CPU oracle (test infrastructure only).
+
+The pages reach long contexts in small memory with a quantised KV cache (Lucebox-Hub
+review, section "2. DFlash", 256K context with a compressed cache); they do not define a
+format, so this one is self-defined and written to be exact where it matters:
+
+* Codes: OCP 8-bit floating point E4M3 (1 sign bit, 4 exponent bits with bias 7, 3
+  mantissa bits; subnormals at exponent field 0; largest finite value 448; the pattern
+  S.1111.111 is NaN and never produced here). Encoding rounds to nearest, ties to even.
+* Scale: one power of two per (token, KV head) row of D values: the smallest 2^e with
+  max|x| <= 448 * 2^e (2^0 for an all-zero row). x / 2^e is then exact and within range,
+  so a code is the E4M3 rounding of an exactly known number.
+* Dequantisation: code value * 2^e, exactly representable in bfloat16 (at most 4
+  significant bits, exponent well inside range), so an attention kernel that widens codes
+  to bf16 sees exactly the values this oracle uses.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .tree_verify import bf16_bits_to_f64
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """float64 values of E4M3 codes (uint8). NaN codes decode to NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * 2.0 ** (e - 7))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return s * val
+
+
+def _e4m3_table():
+    codes = np.arange(0, 0x7F, dtype=np.uint8)          # non-negative finite codes 0 .. 0x7E
+    return codes, e4m3_decode(codes)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Round float64 values with |x| <= 448 to the nearest E4M3 code, ties to the even code.
+
+    Written as a search over the 127 non-negative finite code values (plain and slow): the
+    nearest value wins; at an exact midpoint the code with an even mantissa field (lowest
+    bit 0) wins."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.abs(x) > E4M3_MAX) or np.any(~np.isfinite(x)):
+        raise ValueError("values must be finite with |x| <= 448")
+    codes, vals = _e4m3_table()
+    a = np.abs(x).ravel()
+    idx = np.searchsorted(vals, a)                        # vals[idx-1] < a <= vals[idx]
+    hi = np.clip(idx, 0, len(vals) - 1)
+    lo = np.clip(idx - 1, 0, len(vals) - 1)
+    d_hi, d_lo = vals[hi] - a, a - vals[lo]
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((codes[hi] & 1) == 0))
+    out = np.where(pick_hi, codes[hi], codes[lo]).astype(np.uint8)
+    out = np.where(a == 0, 0, out).astype(np.uint8)
+    sign = (x.ravel() < 0) & (out != 0)
+    out = out | np.where(sign, 0x80, 0).astype(np.uint8)
+    return out.reshape(x.shape)
+
+
+def row_scale_exponent(amax: float) -> int:
+    """Smallest e with amax <= 448 * 2^e (0 for amax == 0), by exact exponent arithmetic."""
+    if amax == 0:
+        return 0
+    m, k = math.frexp(amax)            # amax = m * 2^k, 0.5 <= m < 1; 448 = 0.875 * 2^9
+    return k - 9 if m <= 0.875 else k - 8
+
+
+def quantize_kv(bits) -> tuple[np.ndarray, np.ndarray]:
+    """bf16 bits [T, H, D] -> (E4M3 codes uint8 [T, H, D], scale exponents int32 [T, H])."""
+    x = bf16_bits_to_f64(bits)
+    T, H, D = x.shape
+    exps = np.zeros((T, H), dtype=np.int32)
+    codes = np.zeros((T, H, D), dtype=np.uint8)
+    amax = np.abs(x).max(axis=2)
+    for t in range(T):
+        for h in range(H):
+            e = row_scale_exponent(float(amax[t, h]))
+            exps[t, h] = e
+            codes[t, h] = e4m3_encode(np.ldexp(x[t, h], -e))
+    return codes, exps
+
+
+def dequantize_kv(codes, exps) -> np.ndarray:
+    """float64 [T, H, D] = code value * 2^exponent."""
+    return np.ldexp(e4m3_decode(codes), np.asarray(exps, dtype=np.int64)[..., None])
