@@ -190,6 +190,21 @@ def main():
     tv.argmax_accept(logits, parent, draft, tok=tok, out=acc, workspace=am_ws)
     commit_us = timed(lambda: tv.kv_commit(K[1], Vc[1], L, acc[0], acc[1]))
 
+    # FP8 cache: the caches of the first four layers quantised on the GPU (together larger
+    # than the last-level cache), then the tree attention over them in turn.
+    nf8 = min(layers, 4)
+    f8 = [(tv.kv_quantize_fp8(K[b]), tv.kv_quantize_fp8(Vc[b])) for b in range(nf8)]
+    quant_us = timed(lambda: tv.kv_quantize_fp8(K[1], codes=f8[1][0][0], exps=f8[1][0][1]))
+    f8_turn = [0]
+
+    def fp8_call():
+        (kc, ke), (vc, ve) = f8[f8_turn[0] % nf8]
+        f8_turn[0] += 1
+        tv.tree_attn_fp8(q, kc, vc, ke, ve, parent, L=L, scale=w.scale, num_splits=args.splits, out=out,
+                         workspace=ws)
+    fp8_us = timed(fp8_call, reps=8 * nf8)
+    del f8
+
     attn_ms = np.array([e[0].elapsed_time(e[1]) for e in events]) / layers
     tokens_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
     t_attn_us = float(np.median(attn_ms) * 1e3)
@@ -283,7 +298,8 @@ def main():
                          "attn_p10": round(float(np.percentile(attn_ms, 10) * 1e3), 2),
                          "attn_p90": round(float(np.percentile(attn_ms, 90) * 1e3), 2)},
         "graph_ms_per_step": round(graph_ms_per_step, 3),
-        "next_rows_us": {"sample_accept_T1": round(sample_us, 2), "kv_commit": round(commit_us, 2)},
+        "next_rows_us": {"sample_accept_T1": round(sample_us, 2), "kv_commit": round(commit_us, 2),
+                         "tree_attn_fp8": round(fp8_us, 2), "kv_quantize_fp8_one_tensor": round(quant_us, 2)},
         "kv_gbps": round(kv_gbps, 1),
         "kv_hbm_frac": round(kv_gbps / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -16,10 +16,12 @@ from .tv import (  # noqa: F401
     argmax_workspace,
     argmax_workspace_size,
     kv_commit,
+    kv_quantize_fp8,
     lib,
     sample_accept,
     status_string,
     tree_attn,
+    tree_attn_fp8,
     tree_attn_workspace_size,
     tree_prep,
     validate_tree_host,

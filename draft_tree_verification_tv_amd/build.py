@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(REPO_ROOT, "include")
 LIB_DIR = os.path.join(PKG_DIR, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libtv.so")
-SOURCES = ["tv_api.hip", "tv_attn.hip", "tv_argmax.hip", "tv_tree.hip", "tv_commit.hip"]
+SOURCES = ["tv_api.hip", "tv_attn.hip", "tv_argmax.hip", "tv_tree.hip", "tv_commit.hip", "tv_kvquant.hip"]
 ARCH = "gfx950"
 # Per-file extras. Attention never produces or consumes NaN on valid input (masking uses
 # -inf, which stays honoured), so fmaxf needs no NaN canonicalisation there; the argmax

@@ -92,6 +92,31 @@ int tv_tree_attn(const void* q, const void* k, const void* v, int64_t kv_stride_
                                         lse, workspace, dev_error, static_cast<hipStream_t>(stream)));
 }
 
+int tv_tree_attn_fp8(const void* q, const void* k_codes, const void* v_codes, const int32_t* k_exps,
+                     const int32_t* v_exps, int64_t kv_stride_t, int64_t kv_stride_h, const int32_t* parent,
+                     int N, int L, int Hq, int Hkv, int D, float scale, int num_splits, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream) {
+  if (!q || !k_codes || !v_codes || !k_exps || !v_exps || !parent || !out) return TV_ERR_INVALID_ARG;
+  if (!attn_args_ok(N, L, Hq, Hkv, num_splits)) return TV_ERR_INVALID_ARG;
+  if (D != TV_HEAD_DIM) return TV_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return TV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(out)) return TV_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(k_exps) & 3u) || (reinterpret_cast<uintptr_t>(v_exps) & 3u))
+    return TV_ERR_INVALID_ARG;
+  if (kv_stride_t < 0 || kv_stride_h < 0 || kv_stride_t % 16 || kv_stride_h % 16) return TV_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return TV_ERR_INVALID_ARG;
+  // One KV head's code rows and the exponent arrays must be addressable with 32-bit
+  // byte offsets.
+  if (((int64_t)L + N) * kv_stride_t + 4096 > (int64_t)UINT32_MAX) return TV_ERR_UNSUPPORTED;
+  if (((int64_t)L + N) * Hkv * 4 > (int64_t)UINT32_MAX) return TV_ERR_UNSUPPORTED;
+  const tv::AttnPlan p = tv::attn_plan(N, L, Hq, Hkv, num_splits, cu_count());
+  const size_t need = tv::attn_workspace_bytes(p, Hkv);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return TV_ERR_WORKSPACE;
+  return status_of(tv::launch_tree_attn_fp8(p, q, k_codes, v_codes, k_exps, v_exps, kv_stride_t, kv_stride_h,
+                                            parent, N, L, Hq, Hkv, scale, out, lse, workspace, dev_error,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 size_t tv_argmax_workspace_size(int N, int V) {
   if (N < 1 || V < 1 || V >= INT32_MAX) return 0;
   return tv::argmax_workspace_bytes(N, V);
@@ -158,6 +183,21 @@ int tv_sample_accept(const void* logits, int dtype, int N, int V, int64_t row_st
   return status_of(tv::launch_sample_accept(logits, dtype, N, V, row_stride, temperature, seed, offset, parent,
                                             draft, tok, accept_len, accept_nodes, accept_tokens, bonus, workspace,
                                             dev_error, static_cast<hipStream_t>(stream)));
+}
+
+int tv_kv_quantize_fp8(const void* src, int64_t src_stride_t, int64_t src_stride_h, int T, int Hkv, int D,
+                       void* codes, int64_t codes_stride_t, int64_t codes_stride_h, int32_t* exps, void* stream) {
+  if (!src || !codes || !exps) return TV_ERR_INVALID_ARG;
+  if (T < 0 || Hkv < 1 || (int64_t)T * Hkv > INT32_MAX - 4) return TV_ERR_INVALID_ARG;
+  if (D != TV_HEAD_DIM) return TV_ERR_UNSUPPORTED;
+  if (src_stride_t < (int64_t)Hkv * D || src_stride_h < D || src_stride_t % 2 || src_stride_h % 2)
+    return TV_ERR_INVALID_ARG;
+  if (codes_stride_t < (int64_t)Hkv * D || codes_stride_h < D || codes_stride_t % 2 || codes_stride_h % 2)
+    return TV_ERR_INVALID_ARG;
+  if (((uintptr_t)src % 4) || ((uintptr_t)codes % 2) || ((uintptr_t)exps % 4)) return TV_ERR_INVALID_ARG;
+  if (T == 0) return TV_OK;
+  return status_of(tv::launch_kv_quantize(src, src_stride_t, src_stride_h, T, Hkv, codes, codes_stride_t,
+                                          codes_stride_h, exps, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

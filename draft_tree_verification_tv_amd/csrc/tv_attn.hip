@@ -39,6 +39,13 @@
 //     the workgroups whose range reaches them.
 //   * Work items are remapped so that consecutive ones (the splits of one KV head) land
 //     on the same XCD.
+//   * FP8 cache (E4M3 codes with one power-of-two exponent per token and head; the
+//     quantised KV cache of Lucebox-Hub review, "2. DFlash", in a self-defined format).
+//     Codes and exponents stream into a ring of raw stages (half the HBM bytes of bf16);
+//     each tile is widened once per workgroup into bf16 stages with the same swizzles,
+//     code * 2^e exactly (v_cvt_scalef32_pk_bf16_fp8), two steps ahead for K and one for
+//     V, inside the same one-barrier-per-tile pipeline. The MFMA and softmax code is
+//     shared with the bf16 kernel, so both compute the same function of the bf16 values.
 #include <cmath>
 
 #include "tv_internal.h"
@@ -57,6 +64,21 @@ constexpr int NSTAGE = 4;                      // LDS ring: tiles t-1 .. t+2
 constexpr int TREE_ANC_BYTES = kMaxNodes * kAncWords * 8;
 constexpr int TREE_BYTES = TREE_ANC_BYTES + 2 * kMaxNodes * 4;
 constexpr int SMEM_BYTES = NSTAGE * STAGE_B + TREE_BYTES;
+// FP8 cache: raw stages of [K codes 8 KB][V codes 8 KB][K exps 256 B][V exps 256 B], then
+// three bf16 K stages, two bf16 V stages, the tree masks.
+constexpr int F8_ROWB = D;                                  // bytes per code row
+constexpr int F8_TILE_B = KT * F8_ROWB;                     // 8 KB
+constexpr int F8_RAW_B = 2 * F8_TILE_B + 2 * KT * 4;
+constexpr int F8_NRAW = 4;
+constexpr int F8_KB_OFF = F8_NRAW * F8_RAW_B;
+constexpr int F8_VB_OFF = F8_KB_OFF + 3 * TILE_B;
+constexpr int F8_TREE_OFF = F8_VB_OFF + 2 * TILE_B;
+constexpr int F8_SMEM_BYTES = F8_TREE_OFF + TREE_BYTES;
+static_assert(F8_SMEM_BYTES <= 160 * 1024, "FP8 stages exceed the LDS");
+// Row exponents for which every code * 2^e is a normal bf16 (or zero) and 2^e a normal
+// fp32: smallest code 2^-9, largest 448.
+constexpr int kExpMin = -117;
+constexpr int kExpMax = 119;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleTh = 8.0f;
@@ -65,8 +87,11 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 struct SplitParams {
   const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
+  const void* k;   // bf16 values, or E4M3 codes
+  const void* v;
+  const int32_t* ek;  // FP8 only: row exponents [T][Hkv]
+  const int32_t* ev;
+  int Hkv;
   int64_t st, sh;  // KV strides in elements
   const int32_t* parent;
   int N, L, T, Hq, G, M;
@@ -109,6 +134,29 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t goff, const void* g
       : "memory");
 }
 
+// The same with 4 bytes per lane (lane i lands at lds + 4*i).
+__device__ __forceinline__ void dma4(uint32_t lds, uint32_t goff, const void* gbase) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(goff), "s"(gbase)
+      : "memory");
+}
+
+// A pointer whose value is the same in every lane, moved to scalar registers.
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* ptr) {
+  const uint64_t x = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
 // Workgroup barrier that waits for this wave's LDS traffic and for all but its newest
 // kPending vector-memory operations (the copies of the tile after next stay in flight).
 // No release fence: outstanding global loads are deliberately not drained.
@@ -117,16 +165,20 @@ __device__ __forceinline__ void barrier_keep(void) {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(kPending) : "memory");
 }
 
-template <int NW>
+template <int NW, bool kF8>
 __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
-  constexpr int BLK = KT / 4;            // 1 KB blocks per K (or V) tile
-  constexpr int BPW = BLK / NW;          // blocks of each per wave
-  constexpr int DPT = 2 * BPW;           // copies per wave per tile
+  // Copies per wave per tile: bf16, 16 blocks of 1 KB for each of K and V; FP8, 8 blocks
+  // of codes for each plus one copy of 128 / NW exponents.
+  constexpr int BLK = kF8 ? KT / 8 : KT / 4;
+  constexpr int BPW = BLK / NW;
+  constexpr int DPT = 2 * BPW + (kF8 ? 1 : 0);
+  constexpr int EPW = 2 * KT / NW;      // FP8: exponents copied per wave
+  constexpr int TREE_OFF = kF8 ? F8_TREE_OFF : NSTAGE * STAGE_B;
   static_assert(BLK % NW == 0, "waves must divide the tile");
 
   extern __shared__ __align__(16) char smem[];
-  uint64_t* anc = reinterpret_cast<uint64_t*>(smem + NSTAGE * STAGE_B);
-  int* par = reinterpret_cast<int*>(smem + NSTAGE * STAGE_B + TREE_ANC_BYTES);
+  uint64_t* anc = reinterpret_cast<uint64_t*>(smem + TREE_OFF);
+  int* par = reinterpret_cast<int*>(smem + TREE_OFF + TREE_ANC_BYTES);
   int* jmp = par + kMaxNodes;
 
   // ---- work item
@@ -169,8 +221,9 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
   const int ntiles = (kend - kbeg + KT - 1) / KT;
   if (kend > p.L) tree_prep_lds(p.parent, p.N, anc, par, jmp, p.dev_error);
 
-  const uint16_t* kbase = p.k + (int64_t)h * p.sh;
-  const uint16_t* vbase = p.v + (int64_t)h * p.sh;
+  constexpr int ESZ = kF8 ? 1 : 2;  // bytes per cache element
+  const char* kb8 = static_cast<const char*>(p.k) + (int64_t)h * p.sh * ESZ;
+  const char* vb8 = static_cast<const char*>(p.v) + (int64_t)h * p.sh * ESZ;
 
   // ---- per-lane LDS offsets
   int koff[8];  // K row ql, chunk 2*s8 + grp
@@ -187,24 +240,63 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
     }
   }
 
-  // ---- HBM -> LDS copies. A tile's K (and V) is 16 blocks of 4 rows x 256 bytes; wave w
-  // copies blocks w, w + NW, ... of both. Lane i of a block copy fills LDS row
+  // ---- HBM -> LDS copies. bf16: a tile's K (and V) is 16 blocks of 4 rows x 256 bytes;
+  // wave w copies blocks w, w + NW, ... of both. Lane i of a block copy fills LDS row
   // 4b + i/16, physical chunk i%16, so it loads logical chunk (i%16) ^ swizzle(row).
+  // FP8: 8 blocks of 8 rows x 128 bytes each, unswizzled (lane i: row 8b + i/8, chunk
+  // i%8); wave w also copies exponents (w % (NW/2)) * EPW .. + EPW - 1 of the tile, of K
+  // for the first half of the waves and of V for the second.
   // Offsets within one KV head are 32-bit (the host guarantees (L+N) rows fit).
-  const char* kb8 = reinterpret_cast<const char*>(kbase);
-  const char* vb8 = reinterpret_cast<const char*>(vbase);
-  const uint32_t rowstride_b = (uint32_t)p.st * 2u;
+  const uint32_t rowstride_b = (uint32_t)p.st * (uint32_t)ESZ;
   const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
   uint32_t dk[BPW], dv[BPW];
 #pragma unroll
   for (int j = 0; j < BPW; ++j) {
-    const int row = 4 * (wave + j * NW) + (lane >> 4);
-    const int pc = lane & 15;
-    dk[j] = (uint32_t)row * rowstride_b + (uint32_t)((pc ^ swz_k(row)) << 4);
-    dv[j] = (uint32_t)row * rowstride_b + (uint32_t)((pc ^ swz_v(row)) << 4);
+    if constexpr (kF8) {
+      const int row = 8 * (wave + j * NW) + (lane >> 3);
+      dk[j] = dv[j] = (uint32_t)row * rowstride_b + (uint32_t)((lane & 7) << 4);
+    } else {
+      const int row = 4 * (wave + j * NW) + (lane >> 4);
+      const int pc = lane & 15;
+      dk[j] = (uint32_t)row * rowstride_b + (uint32_t)((pc ^ swz_k(row)) << 4);
+      dv[j] = (uint32_t)row * rowstride_b + (uint32_t)((pc ^ swz_v(row)) << 4);
+    }
+  }
+  const int32_t* ebase = nullptr;
+  int ekey = 0;  // exponent copied by this lane
+  if constexpr (kF8) {
+    ebase = uniform_ptr(wave < NW / 2 ? p.ek : p.ev);
+    ekey = (wave % (NW / 2)) * EPW + lane;
   }
 
-  auto issue = [&](int t) __attribute__((always_inline)) {
+  auto issue_f8 = [&](int t) __attribute__((always_inline)) {
+    const int kt0 = kbeg + t * KT;
+    const uint32_t raw = lds_base + (uint32_t)((t & (F8_NRAW - 1)) * F8_RAW_B);
+    if (kt0 + KT <= p.T) {
+      const uint32_t base = (uint32_t)kt0 * rowstride_b;
+#pragma unroll
+      for (int j = 0; j < BPW; ++j) {
+        const uint32_t blk = (uint32_t)((wave + j * NW) * 1024);
+        dma16(raw + blk, base + dk[j], kb8);
+        dma16(raw + F8_TILE_B + blk, base + dv[j], vb8);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < BPW; ++j) {
+        const int row = 8 * (wave + j * NW) + (lane >> 3);
+        const uint32_t off = (uint32_t)min(kt0 + row, p.T - 1) * rowstride_b + (uint32_t)((lane & 7) << 4);
+        const uint32_t blk = (uint32_t)((wave + j * NW) * 1024);
+        dma16(raw + blk, off, kb8);
+        dma16(raw + F8_TILE_B + blk, off, vb8);
+      }
+    }
+    if (lane < EPW) {
+      const uint32_t key = (uint32_t)min(kt0 + ekey, p.T - 1);
+      dma4(raw + 2 * F8_TILE_B + wave * EPW * 4, (key * (uint32_t)p.Hkv + (uint32_t)h) * 4u, ebase);
+    }
+  };
+
+  auto issue_bf16 = [&](int t) __attribute__((always_inline)) {
     const int kt0 = kbeg + t * KT;
     const uint32_t st_lds = lds_base + (uint32_t)((t & (NSTAGE - 1)) * STAGE_B);
     if (kt0 + KT <= p.T) {
@@ -228,6 +320,12 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
       }
     }
   };
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    if constexpr (kF8)
+      issue_f8(t);
+    else
+      issue_bf16(t);
+  };
 
   f32x16 o[4];
 #pragma unroll
@@ -239,19 +337,33 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
 
   // Scheduling masks for __builtin_amdgcn_sched_group_barrier.
 
-  // S^T of 32-key block kb of the tile in `stage` into sc[c]: 8 K fragments, 8 MFMAs.
-  auto qk = [&](int stage, int kb, int c) __attribute__((always_inline)) {
-    const char* Ks = smem + stage * STAGE_B + kb * 32 * ROWB;
+  // bf16 tiles of tile t in LDS.
+  auto kstage = [&](int t) __attribute__((always_inline)) -> const char* {
+    if constexpr (kF8)
+      return smem + F8_KB_OFF + (t % 3) * TILE_B;
+    else
+      return smem + (t & (NSTAGE - 1)) * STAGE_B;
+  };
+  auto vstage = [&](int t) __attribute__((always_inline)) -> const char* {
+    if constexpr (kF8)
+      return smem + F8_VB_OFF + (t & 1) * TILE_B;
+    else
+      return smem + (t & (NSTAGE - 1)) * STAGE_B + TILE_B;
+  };
+
+  // S^T of 32-key block kb of tile t into sc[c]: 8 K fragments, 8 MFMAs.
+  auto qk = [&](int t, int kb, int c) __attribute__((always_inline)) {
+    const char* Ks = kstage(t) + kb * 32 * ROWB;
     sc[c] = f32x16{};
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8)
       sc[c] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + koff[s8]), qf[s8], sc[c]);
   };
 
-  // O^T += V^T P^T over 32-key block kb of the tile in `stage`; V^T fragments come from
-  // the row-major V tile through transposed reads (two per MFMA).
-  auto pv = [&](int stage, int kb) __attribute__((always_inline)) {
-    const char* Vs = smem + stage * STAGE_B + TILE_B + kb * 32 * ROWB;
+  // O^T += V^T P^T over 32-key block kb of tile t; V^T fragments come from the row-major
+  // V tile through transposed reads (two per MFMA).
+  auto pv = [&](int t, int kb) __attribute__((always_inline)) {
+    const char* Vs = vstage(t) + kb * 32 * ROWB;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const char* a0 = Vs + (i >> 2) * 16 * ROWB + voff[i & 3];
@@ -346,13 +458,84 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
   auto sub = [&](int t, auto kbc, int tn) __attribute__((always_inline)) {
     constexpr int kb = decltype(kbc)::value;
     constexpr int kbn = kb ^ 1;
-    qk(tn & (NSTAGE - 1), kbn, kbn);
+    qk(tn, kbn, kbn);
     probs(kb);
-    pv(t & (NSTAGE - 1), kb);
+    pv(t, kb);
     if (tn >= nplain) mask(kbeg + tn * KT + kbn * 32, kbn);
     rescale(kbn);
   };
 
+  // FP8: widen the K (or V) codes of raw tile t into its bf16 stage. Thread i converts
+  // 16 codes (row i/8, dims 16*(i%8) ..) with the row's scale 2^e and writes the two bf16
+  // chunks to their swizzled places. Exponents outside [kExpMin, kExpMax] are clamped and
+  // reported.
+  bool bad_exp = false;
+  auto widen = [&](int t, bool is_v) __attribute__((always_inline)) {
+    const char* raw = smem + (t & (F8_NRAW - 1)) * F8_RAW_B + (is_v ? F8_TILE_B : 0);
+    const int* ex = reinterpret_cast<const int*>(smem + (t & (F8_NRAW - 1)) * F8_RAW_B + 2 * F8_TILE_B) +
+                    (is_v ? KT : 0);
+    char* dst = const_cast<char*>(is_v ? vstage(t) : kstage(t));
+#pragma unroll
+    for (int pass = 0; pass < 8 / NW; ++pass) {
+      const int idx = pass * NW * 64 + tid;
+      const int row = idx >> 3, c8 = idx & 7;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(raw + row * F8_ROWB + c8 * 16);
+      int e = ex[row];
+      bad_exp |= e < kExpMin || e > kExpMax;
+      e = min(max(e, kExpMin), kExpMax);
+      const float sc = __int_as_float((e + 127) << 23);
+      u32x4 lo, hi;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        lo[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j], sc, false));
+        lo[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j], sc, true));
+        hi[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j + 2], sc, false));
+        hi[2 * j + 1] =
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j + 2], sc, true));
+      }
+      const int sw = is_v ? swz_v(row) : swz_k(row);
+      *reinterpret_cast<u32x4*>(dst + row * ROWB + (((2 * c8) ^ sw) << 4)) = lo;
+      *reinterpret_cast<u32x4*>(dst + row * ROWB + (((2 * c8 + 1) ^ sw) << 4)) = hi;
+    }
+  };
+
+  if constexpr (kF8) {
+    // ---- FP8 prologue: raw tiles 0..3 start streaming; 0..2 must land. K of tiles 0, 1
+    // and V of tile 0 are widened; the LDS barrier publishes them.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    for (int t = 0; t < 4 && t < ntiles; ++t) issue(t);
+    if (ntiles > 3)
+      barrier_keep<DPT>();
+    else
+      barrier_keep<0>();
+    widen(0, false);
+    if (ntiles > 1) widen(1, false);
+    widen(0, true);
+    if (ntiles > 3)
+      barrier_keep<DPT>();
+    else
+      barrier_keep<0>();
+    qk(0, 0, 0);
+    if (nplain == 0) mask(kbeg, 0);
+    rescale(0);
+
+    // Step t: raw tile t+4 starts (into the stage of raw tile t, fully widened by step
+    // t-1); K of tile t+2 and V of tile t+1 are widened (their raw tiles landed by the
+    // previous barrier; their bf16 stages last held K of tile t-1 and V of tile t-1);
+    // tile t is consumed. The barrier guarantees raw tile t+3 and keeps t+4 in flight.
+    for (int t = 0; t + 1 < ntiles; ++t) {
+      if (t + 4 < ntiles) issue(t + 4);
+      if (t + 2 < ntiles) widen(t + 2, false);
+      widen(t + 1, true);
+      sub(t, std::integral_constant<int, 0>{}, t);
+      sub(t, std::integral_constant<int, 1>{}, t + 1);
+      if (t + 4 < ntiles)
+        barrier_keep<DPT>();
+      else
+        barrier_keep<0>();
+    }
+    if (__any(bad_exp) && lane == 0 && p.dev_error) *p.dev_error = TV_ERR_INVALID_ARG;
+  } else {
   // ---- prologue: tiles 0, 1, 2 start streaming; tiles 0 and 1 must land.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // query loads are not tile copies
   for (int t = 0; t < 3 && t < ntiles; ++t) issue(t);
@@ -373,11 +556,12 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
     sub(t, std::integral_constant<int, 1>{}, t + 1);
     wait_step(t);
   }
+  }
   {
     const int t = ntiles - 1;
     sub(t, std::integral_constant<int, 0>{}, t);
     probs(1);
-    pv(t & (NSTAGE - 1), 1);
+    pv(t, 1);
   }
 
   // ---- partial result of this split
@@ -462,16 +646,17 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams mp) {
   if (mp.lse && lane == 0) mp.lse[row] = mx == -INFINITY ? -INFINITY : (mx + __log2f(wsum)) * kLn2;
 }
 
-template <int NW>
+template <int NW, bool kF8>
 hipError_t launch_split(const SplitParams& sp, int nwg, hipStream_t stream) {
+  constexpr int smem = kF8 ? F8_SMEM_BYTES : SMEM_BYTES;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_split_kernel<NW>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, SMEM_BYTES);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_split_kernel<NW, kF8>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(attn_split_kernel<NW>, dim3(nwg), dim3(NW * 64), SMEM_BYTES, stream, sp);
+  hipLaunchKernelGGL((attn_split_kernel<NW, kF8>), dim3(nwg), dim3(NW * 64), smem, stream, sp);
   return hipGetLastError();
 }
 
@@ -511,9 +696,12 @@ size_t attn_workspace_bytes(const AttnPlan& p, int Hkv) {
   return (bytes + 255) / 256 * 256;
 }
 
-hipError_t launch_tree_attn(const AttnPlan& plan, const void* q, const void* k, const void* v, int64_t st,
-                            int64_t sh, const int32_t* parent, int N, int L, int Hq, int Hkv, float scale,
-                            void* out, float* lse, void* workspace, int32_t* dev_error, hipStream_t stream) {
+namespace {
+
+hipError_t launch_attn(const AttnPlan& plan, bool f8, const void* q, const void* k, const void* v,
+                       const int32_t* ek, const int32_t* ev, int64_t st, int64_t sh, const int32_t* parent, int N,
+                       int L, int Hq, int Hkv, float scale, void* out, float* lse, void* workspace,
+                       int32_t* dev_error, hipStream_t stream) {
   const size_t rows = (size_t)Hkv * plan.RT * plan.S * TILE_ROWS;
   char* ws = static_cast<char*>(workspace);
   float* part_o = reinterpret_cast<float*>(ws);
@@ -521,8 +709,11 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const void* q, const void* k, 
 
   SplitParams sp;
   sp.q = static_cast<const uint16_t*>(q);
-  sp.k = static_cast<const uint16_t*>(k);
-  sp.v = static_cast<const uint16_t*>(v);
+  sp.k = k;
+  sp.v = v;
+  sp.ek = ek;
+  sp.ev = ev;
+  sp.Hkv = Hkv;
   sp.st = st;
   sp.sh = sh;
   sp.parent = parent;
@@ -543,10 +734,18 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const void* q, const void* k, 
   sp.remap = (nwg % 8 == 0) ? 1 : 0;
 
   hipError_t e;
-  switch (plan.NW) {
-    case 2: e = launch_split<2>(sp, nwg, stream); break;
-    case 4: e = launch_split<4>(sp, nwg, stream); break;
-    default: e = launch_split<8>(sp, nwg, stream); break;
+  if (f8) {
+    switch (plan.NW) {
+      case 2: e = launch_split<2, true>(sp, nwg, stream); break;
+      case 4: e = launch_split<4, true>(sp, nwg, stream); break;
+      default: e = launch_split<8, true>(sp, nwg, stream); break;
+    }
+  } else {
+    switch (plan.NW) {
+      case 2: e = launch_split<2, false>(sp, nwg, stream); break;
+      case 4: e = launch_split<4, false>(sp, nwg, stream); break;
+      default: e = launch_split<8, false>(sp, nwg, stream); break;
+    }
   }
   if (e != hipSuccess) return e;
 
@@ -563,6 +762,23 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const void* q, const void* k, 
   const int rows_out = N * Hq;
   hipLaunchKernelGGL(attn_merge_kernel, dim3((rows_out + 3) / 4), dim3(256), 0, stream, mp);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_tree_attn(const AttnPlan& plan, const void* q, const void* k, const void* v, int64_t st,
+                            int64_t sh, const int32_t* parent, int N, int L, int Hq, int Hkv, float scale,
+                            void* out, float* lse, void* workspace, int32_t* dev_error, hipStream_t stream) {
+  return launch_attn(plan, false, q, k, v, nullptr, nullptr, st, sh, parent, N, L, Hq, Hkv, scale, out, lse,
+                     workspace, dev_error, stream);
+}
+
+hipError_t launch_tree_attn_fp8(const AttnPlan& plan, const void* q, const void* kc, const void* vc,
+                                const int32_t* ek, const int32_t* ev, int64_t st, int64_t sh,
+                                const int32_t* parent, int N, int L, int Hq, int Hkv, float scale, void* out,
+                                float* lse, void* workspace, int32_t* dev_error, hipStream_t stream) {
+  return launch_attn(plan, true, q, kc, vc, ek, ev, st, sh, parent, N, L, Hq, Hkv, scale, out, lse, workspace,
+                     dev_error, stream);
 }
 
 }  // namespace tv

@@ -25,7 +25,8 @@ HEAD_DIM = 128
 
 EXPORTS = ("tv_abi_version", "tv_status_string", "tv_validate_tree_host", "tv_tree_prep",
            "tv_tree_attn_workspace_size", "tv_tree_attn", "tv_argmax_workspace_size",
-           "tv_argmax", "tv_accept", "tv_argmax_accept", "tv_sample_accept", "tv_kv_commit")
+           "tv_argmax", "tv_accept", "tv_argmax_accept", "tv_sample_accept", "tv_kv_commit",
+           "tv_kv_quantize_fp8", "tv_tree_attn_fp8")
 
 
 class TVError(RuntimeError):
@@ -78,6 +79,11 @@ def lib():
                                        _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]
         L.tv_kv_commit.restype = _i32
         L.tv_kv_commit.argtypes = [_vp, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
+        L.tv_tree_attn_fp8.restype = _i32
+        L.tv_tree_attn_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
+                                       _i32, _vp, _vp, _vp, _sz, _vp, _vp]
+        L.tv_kv_quantize_fp8.restype = _i32
+        L.tv_kv_quantize_fp8.argtypes = [_vp, _i64, _i64, _i32, _i32, _i32, _vp, _i64, _i64, _vp, _vp]
         if L.tv_abi_version() != 1:
             raise RuntimeError("libtv ABI version mismatch")
         _lib = L
@@ -166,6 +172,48 @@ def tree_attn(q, k, v, parent, L=None, scale=None, num_splits=0, out=None, lse=N
                               Hkv, D, float(scale), int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _ptr(dev_error), _stream(stream)),
            "tv_tree_attn")
+    return out
+
+
+def tree_attn_fp8(q, k_codes, v_codes, k_exps, v_exps, parent, L=None, scale=None, num_splits=0, out=None,
+                  lse=None, workspace=None, dev_error=None, stream=None):
+    """Tree-masked attention over an FP8 cache: k_codes, v_codes uint8 [>= L+N, Hkv, D]
+    (E4M3, last dim contiguous, shared strides); k_exps, v_exps int32 [>= L+N, Hkv]
+    contiguous (row scales 2^e, as kv_quantize_fp8 writes them). Otherwise as tree_attn."""
+    _need_cuda("q", q, torch.bfloat16)
+    for name, t in (("k_codes", k_codes), ("v_codes", v_codes)):
+        _need_cuda(name, t, torch.uint8)
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be 3-D")
+    for name, t in (("k_exps", k_exps), ("v_exps", v_exps)):
+        _need_cuda(name, t, torch.int32)
+        if t.dim() != 2 or not t.is_contiguous() or t.shape[1] != k_codes.shape[1]:
+            raise ValueError(f"{name} must be a contiguous [T, Hkv] tensor")
+    _need_cuda("parent", parent, torch.int32)
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [N, Hq, D] tensor")
+    if k_codes.stride() != v_codes.stride() or k_codes.stride(2) != 1:
+        raise ValueError("k_codes and v_codes must share strides with a contiguous last dim")
+    N, Hq, D = q.shape
+    Hkv = k_codes.shape[1]
+    if L is None:
+        L = k_codes.shape[0] - N
+    rows = L + N
+    if L < 0 or min(k_codes.shape[0], v_codes.shape[0], k_exps.shape[0], v_exps.shape[0]) < rows:
+        raise ValueError("codes and exponents must hold L + N rows")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((N, Hq, D), dtype=torch.bfloat16, device=q.device)
+    ws_bytes = tree_attn_workspace_size(N, L, Hq, Hkv, D, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().tv_tree_attn_fp8(_ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_exps), _ptr(v_exps),
+                                  k_codes.stride(0), k_codes.stride(1), _ptr(parent), N, L, Hq, Hkv, D,
+                                  float(scale), int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _ptr(dev_error),
+                                  _stream(stream)),
+           "tv_tree_attn_fp8")
     return out
 
 
@@ -295,6 +343,31 @@ def kv_commit(k, v, L, accept_len, accept_nodes, N=None, new_len=None, dev_error
     _check(lib().tv_kv_commit(_ptr(k), _ptr(v), k.stride(0), k.stride(1), k.shape[1], k.shape[2], L, N,
                               _ptr(accept_len), _ptr(accept_nodes), _ptr(new_len), _ptr(dev_error), _stream(stream)),
            "tv_kv_commit")
+
+
+def kv_quantize_fp8(x, codes=None, exps=None, stream=None):
+    """Quantise a bf16 cache x [T, Hkv, D] (last dim contiguous) to E4M3 codes (uint8,
+    same shape) and one power-of-two exponent per (token, head) row (int32 [T, Hkv]); the
+    row dequantises to code * 2^exp. Returns (codes, exps)."""
+    _need_cuda("x", x, torch.bfloat16)
+    if x.dim() != 3 or (x.numel() and x.stride(2) != 1):
+        raise ValueError("x must be [T, Hkv, D] with a contiguous last dim")
+    T, H, D = x.shape
+    if codes is None:
+        codes = torch.empty((T, H, D), dtype=torch.uint8, device=x.device)
+    if exps is None:
+        exps = torch.empty((T, H), dtype=torch.int32, device=x.device)
+    _need_cuda("codes", codes, torch.uint8)
+    _need_cuda("exps", exps, torch.int32)
+    if codes.shape != x.shape or tuple(exps.shape) != (T, H) or not exps.is_contiguous():
+        raise ValueError("codes must be [T, Hkv, D] (contiguous last dim), exps a contiguous [T, Hkv]")
+    if T == 0:
+        return codes, exps
+    if codes.stride(2) != 1:
+        raise ValueError("codes must have a contiguous last dim")
+    _check(lib().tv_kv_quantize_fp8(_ptr(x), x.stride(0), x.stride(1), T, H, D, _ptr(codes), codes.stride(0),
+                                    codes.stride(1), _ptr(exps), _stream(stream)), "tv_kv_quantize_fp8")
+    return codes, exps
 
 
 def verify(q, k, v, parent, logits, draft, L=None, scale=None, num_splits=0, attn_workspace=None,

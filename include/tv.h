@@ -20,6 +20,8 @@
  *   tv_argmax_accept   the two above in one call
  *   tv_sample_accept   the same with sampled targets (temperature > 0)
  *   tv_kv_commit  moves the accepted nodes' K/V rows behind the context   (bit exact)
+ *   tv_kv_quantize_fp8   bf16 cache -> FP8 (E4M3) codes + per-row scales      (bit exact)
+ *   tv_tree_attn_fp8     tree attention over that FP8 cache
  *
  * Conventions shared by every call
  *   - Pointers are DEVICE pointers unless the name ends in _host. The caller owns every
@@ -116,6 +118,31 @@ int tv_tree_attn(const void* q, const void* k, const void* v, int64_t kv_stride_
                  void* stream);
 
 /*
+ * Tree attention over an FP8 key/value cache (the quantised cache of Lucebox-Hub review,
+ * section "2. DFlash"; format of tv_kv_quantize_fp8). Computes tv_tree_attn on the
+ * dequantised cache k[t][h][d] = decode(k_codes[t][h][d]) * 2^k_exps[t * Hkv + h] (and
+ * likewise v), which is exact in bf16: the result is the bf16 call's on those values.
+ *   k_codes, v_codes   uint8 E4M3 codes; element (t, kvh, d) at base + t*kv_stride_t +
+ *                      kvh*kv_stride_h + d (strides in bytes, multiples of 16; d
+ *                      contiguous; 16-byte aligned base). NaN codes (0x7F, 0xFF) are not
+ *                      allowed.
+ *   k_exps, v_exps     int32 [>= L + N][Hkv], contiguous, 4-byte aligned; each in
+ *                      [-117, 119] (what tv_kv_quantize_fp8 gives for rows whose largest
+ *                      magnitude lies in [2^-125, 2^127]). An exponent outside is clamped
+ *                      into the range and, when dev_error is non-NULL, TV_ERR_INVALID_ARG
+ *                      is stored there.
+ *   The other arguments, the workspace (tv_tree_attn_workspace_size) and the limits are
+ *   those of tv_tree_attn, with (L + N) * kv_stride_t and (L + N) * Hkv * 4 bytes below
+ *   4 GiB.
+ */
+int tv_tree_attn_fp8(const void* q, const void* k_codes, const void* v_codes,
+                     const int32_t* k_exps, const int32_t* v_exps, int64_t kv_stride_t,
+                     int64_t kv_stride_h, const int32_t* parent, int N, int L, int Hq,
+                     int Hkv, int D, float scale, int num_splits, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, int32_t* dev_error,
+                     void* stream);
+
+/*
  * Row argmax: tok[i] = the lowest index u with logits[i][u] equal to the row maximum
  * (float comparison, so -0.0 and +0.0 tie). Rows holding NaN give an unspecified index.
  *   logits   dtype TV_BF16 or TV_F32, row i at base + i*row_stride elements.
@@ -199,6 +226,26 @@ int tv_sample_accept(const void* logits, int dtype, int N, int V, int64_t row_st
 int tv_kv_commit(void* k, void* v, int64_t kv_stride_t, int64_t kv_stride_h, int Hkv, int D,
                  int L, int N, const int32_t* accept_len, const int32_t* accept_nodes,
                  int32_t* new_len, int32_t* dev_error, void* stream);
+
+/*
+ * FP8 key/value cache: quantiser. Long contexts fit small memory through a quantised KV
+ * cache (Lucebox-Hub review, section "2. DFlash"); the format is this library's own. Each
+ * (token, head) row of D values gets one exponent e, the smallest integer with
+ * max|x| <= 448 * 2^e (e = 0 for an all-zero row), and each value the OCP E4M3 code
+ * (bias 7, no infinities, largest finite 448) nearest to x * 2^-e, ties to the even
+ * mantissa, -0 coded as +0. The row dequantises to decode(code) * 2^e, which is exact in
+ * bfloat16.
+ *   src          bf16 [T][Hkv][D], strides src_stride_t / src_stride_h in elements (even),
+ *                D contiguous; 4-byte aligned. Values must be finite.
+ *   codes        uint8 [T][Hkv][D] out, strides codes_stride_t / codes_stride_h in bytes
+ *                (even), D contiguous; 2-byte aligned.
+ *   exps         int32 [T * Hkv] out (row t * Hkv + h), 4-byte aligned.
+ * Limits: T >= 0 (T = 0 enqueues nothing), Hkv >= 1, D = TV_HEAD_DIM (else
+ * TV_ERR_UNSUPPORTED), strides at least the packed ones.
+ */
+int tv_kv_quantize_fp8(const void* src, int64_t src_stride_t, int64_t src_stride_h, int T,
+                       int Hkv, int D, void* codes, int64_t codes_stride_t,
+                       int64_t codes_stride_h, int32_t* exps, void* stream);
 
 #ifdef __cplusplus
 }

@@ -73,18 +73,28 @@ def row_scale_exponent(amax: float) -> int:
     return k - 9 if m <= 0.875 else k - 8
 
 
-def quantize_kv(bits) -> tuple[np.ndarray, np.ndarray]:
-    """bf16 bits [T, H, D] -> (E4M3 codes uint8 [T, H, D], scale exponents int32 [T, H])."""
-    x = bf16_bits_to_f64(bits)
-    T, H, D = x.shape
+def row_scale_exponents(amax) -> np.ndarray:
+    """row_scale_exponent over an array of row maxima (frexp is exact in float64)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    m, k = np.frexp(amax)
+    e = np.where(m <= 0.875, k - 9, k - 8)
+    return np.where(amax == 0, 0, e).astype(np.int32)
+
+
+def quantize_kv(bits, chunk_rows: int = 1 << 16) -> tuple[np.ndarray, np.ndarray]:
+    """bf16 bits [T, H, D] -> (E4M3 codes uint8 [T, H, D], scale exponents int32 [T, H]).
+
+    Rows are independent: each is scaled by 2^-e (exact) and encoded; tokens are processed
+    in chunks only to bound memory."""
+    bits = np.asarray(bits)
+    T, H, D = bits.shape
     exps = np.zeros((T, H), dtype=np.int32)
     codes = np.zeros((T, H, D), dtype=np.uint8)
-    amax = np.abs(x).max(axis=2)
-    for t in range(T):
-        for h in range(H):
-            e = row_scale_exponent(float(amax[t, h]))
-            exps[t, h] = e
-            codes[t, h] = e4m3_encode(np.ldexp(x[t, h], -e))
+    for t0 in range(0, T, chunk_rows):
+        x = bf16_bits_to_f64(bits[t0:t0 + chunk_rows])
+        e = row_scale_exponents(np.abs(x).max(axis=2))
+        exps[t0:t0 + chunk_rows] = e
+        codes[t0:t0 + chunk_rows] = e4m3_encode(np.ldexp(x, -e[..., None].astype(np.int64)))
     return codes, exps
 
 

@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_declares_the_documented_calls():
     names = declared_functions()
     for n in ("tv_tree_attn", "tv_argmax", "tv_accept", "tv_argmax_accept", "tv_sample_accept", "tv_kv_commit",
-              "tv_tree_prep", "tv_abi_version", "tv_validate_tree_host"):
+              "tv_kv_quantize_fp8", "tv_tree_attn_fp8", "tv_tree_prep", "tv_abi_version", "tv_validate_tree_host"):
         assert n in names
     assert set(names) == set(tv.EXPORTS)
 
@@ -77,6 +77,28 @@ def attn_call(**kw):
 ])
 def test_tree_attn_rejects(kw, status):
     assert attn_call(**kw) == status
+
+
+def attn_fp8_call(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ek=FAKE, ev=FAKE, st=256, sh=128, parent=FAKE, N=4, L=100, Hq=8, Hkv=2,
+             D=128, scale=0.088, splits=0, out=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 40, err=None, stream=None)
+    a.update(kw)
+    return tv.lib().tv_tree_attn_fp8(a["q"], a["k"], a["v"], a["ek"], a["ev"], a["st"], a["sh"], a["parent"],
+                                     a["N"], a["L"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["splits"], a["out"],
+                                     a["lse"], a["ws"], a["ws_bytes"], a["err"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(ek=None), 1), (dict(ev=None), 1),
+    (dict(parent=None), 1), (dict(out=None), 1), (dict(N=0), 1), (dict(N=257), 1), (dict(L=-1), 1),
+    (dict(Hq=6, Hkv=4), 1), (dict(D=64), 3), (dict(scale=0.0), 1), (dict(st=200), 1), (dict(sh=8), 1),
+    (dict(k=ctypes.c_void_p(0x10008)), 1), (dict(ek=ctypes.c_void_p(0x10002)), 1),
+    (dict(ev=ctypes.c_void_p(0x10001)), 1), (dict(lse=ctypes.c_void_p(0x10002)), 1),
+    (dict(st=1 << 20, L=1 << 12), 3), (dict(Hkv=1 << 20, Hq=1 << 20, L=1 << 12), 3),
+    (dict(ws=None), 4), (dict(ws_bytes=16), 4),
+])
+def test_tree_attn_fp8_rejects(kw, status):
+    assert attn_fp8_call(**kw) == status
 
 
 def test_workspace_sizes():
@@ -199,3 +221,25 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         tv.argmax(torch.zeros(2, 8))
+
+
+# tv_kv_quantize_fp8(src, sst, ssh, T, Hkv, D, codes, cst, csh, exps, stream)
+@pytest.mark.parametrize("args,status", [
+    ((None, 1024, 128, 10, 8, 128, FAKE, 1024, 128, FAKE), 1),
+    ((FAKE, 1024, 128, 10, 8, 128, None, 1024, 128, FAKE), 1),
+    ((FAKE, 1024, 128, 10, 8, 128, FAKE, 1024, 128, None), 1),
+    ((FAKE, 1024, 128, -1, 8, 128, FAKE, 1024, 128, FAKE), 1),
+    ((FAKE, 1024, 128, 10, 0, 128, FAKE, 1024, 128, FAKE), 1),
+    ((FAKE, 1024, 128, 10, 8, 64, FAKE, 1024, 128, FAKE), 3),
+    ((FAKE, 1022, 128, 10, 8, 128, FAKE, 1024, 128, FAKE), 1),
+    ((FAKE, 1024, 126, 10, 8, 128, FAKE, 1024, 128, FAKE), 1),
+    ((FAKE, 1024, 128, 10, 8, 128, FAKE, 1024, 127, FAKE), 1),
+    ((FAKE, 1024, 128, 10, 8, 128, FAKE, 1023, 128, FAKE), 1),
+    ((ctypes.c_void_p(0x10002), 1024, 128, 10, 8, 128, FAKE, 1024, 128, FAKE), 1),
+    ((FAKE, 1024, 128, 10, 8, 128, ctypes.c_void_p(0x10001), 1024, 128, FAKE), 1),
+    ((FAKE, 1024, 128, 10, 8, 128, FAKE, 1024, 128, ctypes.c_void_p(0x10002)), 1),
+    ((FAKE, 1 << 40, 128, 1 << 30, 8, 128, FAKE, 1 << 40, 128, FAKE), 1),
+    ((FAKE, 1024, 128, 0, 8, 128, FAKE, 1024, 128, FAKE), 0),
+])
+def test_kv_quantize_rejects(args, status):
+    assert tv.lib().tv_kv_quantize_fp8(*args, None) == status

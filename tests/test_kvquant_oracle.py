@@ -106,3 +106,23 @@ def test_mutant_round_half_up_is_caught():
     def half_up(v):
         return np.searchsorted(finite, v, side="right").astype(np.uint8)   # always the upper code
     assert not np.array_equal(half_up(mids), oracle.e4m3_encode(mids))
+
+
+def test_row_exponents_vectorised_equal_scalar_and_chunking_is_invisible():
+    rng = np.random.default_rng(4)
+    a = np.concatenate([[0.0, 448.0, 449.0, 224.0, 2.0 ** -130, 3e38],
+                        rng.uniform(0, 1000, 500) * 2.0 ** rng.integers(-60, 60, 500)])
+    vec = oracle.kvquant.row_scale_exponents(a)
+    assert vec.tolist() == [oracle.row_scale_exponent(float(x)) for x in a]
+    x = rng.standard_normal((37, 2, 128)).astype(np.float32) * np.exp2(rng.integers(-8, 8, (37, 2, 1)))
+    bits = bf16_bits_from_f32(x.astype(np.float32))
+    c1, e1 = oracle.quantize_kv(bits)
+    c2, e2 = oracle.quantize_kv(bits, chunk_rows=5)
+    assert np.array_equal(c1, c2) and np.array_equal(e1, e2)
+    # a row at a time through the scalar definitions
+    xf = oracle.bf16_bits_to_f64(bits)
+    for t in (0, 17, 36):
+        for h in range(2):
+            e = oracle.row_scale_exponent(float(np.abs(xf[t, h]).max()))
+            assert e1[t, h] == e
+            assert np.array_equal(c1[t, h], oracle.e4m3_encode(np.ldexp(xf[t, h], -e)))
