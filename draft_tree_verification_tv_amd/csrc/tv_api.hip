@@ -190,11 +190,11 @@ int tv_kv_quantize_fp8(const void* src, int64_t src_stride_t, int64_t src_stride
   if (!src || !codes || !exps) return TV_ERR_INVALID_ARG;
   if (T < 0 || Hkv < 1 || (int64_t)T * Hkv > INT32_MAX - 4) return TV_ERR_INVALID_ARG;
   if (D != TV_HEAD_DIM) return TV_ERR_UNSUPPORTED;
-  if (src_stride_t < (int64_t)Hkv * D || src_stride_h < D || src_stride_t % 2 || src_stride_h % 2)
+  if (src_stride_t < (int64_t)Hkv * D || src_stride_h < D || src_stride_t % 8 || src_stride_h % 8)
     return TV_ERR_INVALID_ARG;
-  if (codes_stride_t < (int64_t)Hkv * D || codes_stride_h < D || codes_stride_t % 2 || codes_stride_h % 2)
+  if (codes_stride_t < (int64_t)Hkv * D || codes_stride_h < D || codes_stride_t % 8 || codes_stride_h % 8)
     return TV_ERR_INVALID_ARG;
-  if (((uintptr_t)src % 4) || ((uintptr_t)codes % 2) || ((uintptr_t)exps % 4)) return TV_ERR_INVALID_ARG;
+  if (!aligned16(src) || ((uintptr_t)codes % 8) || ((uintptr_t)exps % 4)) return TV_ERR_INVALID_ARG;
   if (T == 0) return TV_OK;
   return status_of(tv::launch_kv_quantize(src, src_stride_t, src_stride_h, T, Hkv, codes, codes_stride_t,
                                           codes_stride_h, exps, static_cast<hipStream_t>(stream)));

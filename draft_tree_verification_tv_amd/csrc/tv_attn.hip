@@ -61,6 +61,9 @@ constexpr int ROWB = D * 2;                    // bytes per K or V row (256)
 constexpr int TILE_B = KT * ROWB;              // 16 KB per K (or V) tile
 constexpr int STAGE_B = 2 * TILE_B;            // K + V
 constexpr int NSTAGE = 4;                      // LDS ring: tiles t-1 .. t+2
+// bf16 ring layout: the four K stages first, then the four V stages, so every stage of
+// either lies within 64 KB of its first one (ds_read immediate offsets reach it).
+constexpr int V_OFF = NSTAGE * TILE_B;
 constexpr int TREE_ANC_BYTES = kMaxNodes * kAncWords * 8;
 constexpr int TREE_BYTES = TREE_ANC_BYTES + 2 * kMaxNodes * 4;
 constexpr int SMEM_BYTES = NSTAGE * STAGE_B + TREE_BYTES;
@@ -229,14 +232,17 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
   int koff[8];  // K row ql, chunk 2*s8 + grp
 #pragma unroll
   for (int s8 = 0; s8 < 8; ++s8) koff[s8] = ql * ROWB + (((2 * s8 + grp) ^ swz_k(ql)) << 4);
-  int voff[4];  // V rows 4*grp + i16/4 (+8), head-dim columns db*32 + g16*16 + 4*(i16%4)
+  // V rows 4*grp + i16/4 (+8), head-dim columns db*32 + g16*16 + 4*(i16%4); the offset
+  // of the V stages is included, so the per-stage part fits the ds_read immediate.
+  constexpr int VBASE = kF8 ? F8_VB_OFF : V_OFF;
+  int voff[4];
   {
     const int row = 4 * grp + (i16 >> 2);
     const int sw = swz_v(row);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int chunk = db * 4 + g16 * 2 + ((i16 & 3) >> 1);
-      voff[db] = row * ROWB + ((chunk ^ sw) << 4) + (i16 & 1) * 8;
+      voff[db] = VBASE + row * ROWB + ((chunk ^ sw) << 4) + (i16 & 1) * 8;
     }
   }
 
@@ -298,14 +304,14 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
 
   auto issue_bf16 = [&](int t) __attribute__((always_inline)) {
     const int kt0 = kbeg + t * KT;
-    const uint32_t st_lds = lds_base + (uint32_t)((t & (NSTAGE - 1)) * STAGE_B);
+    const uint32_t st_lds = lds_base + (uint32_t)((t & (NSTAGE - 1)) * TILE_B);
     if (kt0 + KT <= p.T) {
       const uint32_t base = (uint32_t)kt0 * rowstride_b;
 #pragma unroll
       for (int j = 0; j < BPW; ++j) {
         const uint32_t blk = (uint32_t)((wave + j * NW) * 1024);
         dma16(st_lds + blk, base + dk[j], kb8);
-        dma16(st_lds + TILE_B + blk, base + dv[j], vb8);
+        dma16(st_lds + V_OFF + blk, base + dv[j], vb8);
       }
     } else {
       // Last tile of the sequence: rows past L+N re-read row L+N-1 (always masked).
@@ -316,7 +322,7 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
         const uint32_t grow = (uint32_t)min(kt0 + row, p.T - 1) * rowstride_b;
         const uint32_t blk = (uint32_t)((wave + j * NW) * 1024);
         dma16(st_lds + blk, grow + (uint32_t)((pc ^ swz_k(row)) << 4), kb8);
-        dma16(st_lds + TILE_B + blk, grow + (uint32_t)((pc ^ swz_v(row)) << 4), vb8);
+        dma16(st_lds + V_OFF + blk, grow + (uint32_t)((pc ^ swz_v(row)) << 4), vb8);
       }
     }
   };
@@ -342,28 +348,29 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
     if constexpr (kF8)
       return smem + F8_KB_OFF + (t % 3) * TILE_B;
     else
-      return smem + (t & (NSTAGE - 1)) * STAGE_B;
+      return smem + (t & (NSTAGE - 1)) * TILE_B;
   };
+  // V stage of tile t relative to VBASE (pv adds VBASE through voff).
   auto vstage = [&](int t) __attribute__((always_inline)) -> const char* {
     if constexpr (kF8)
-      return smem + F8_VB_OFF + (t & 1) * TILE_B;
+      return smem + (t & 1) * TILE_B;
     else
-      return smem + (t & (NSTAGE - 1)) * STAGE_B + TILE_B;
+      return smem + (t & (NSTAGE - 1)) * TILE_B;
   };
 
-  // S^T of 32-key block kb of tile t into sc[c]: 8 K fragments, 8 MFMAs.
-  auto qk = [&](int t, int kb, int c) __attribute__((always_inline)) {
-    const char* Ks = kstage(t) + kb * 32 * ROWB;
+  // S^T of 32-key block kb of the K tile at Kt into sc[c]: 8 K fragments, 8 MFMAs.
+  auto qk = [&](const char* Kt, int kb, int c) __attribute__((always_inline)) {
+    const char* Ks = Kt + kb * 32 * ROWB;
     sc[c] = f32x16{};
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8)
       sc[c] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + koff[s8]), qf[s8], sc[c]);
   };
 
-  // O^T += V^T P^T over 32-key block kb of tile t; V^T fragments come from the row-major
-  // V tile through transposed reads (two per MFMA).
-  auto pv = [&](int t, int kb) __attribute__((always_inline)) {
-    const char* Vs = vstage(t) + kb * 32 * ROWB;
+  // O^T += V^T P^T over 32-key block kb of the V tile at Vt + VBASE; V^T fragments come
+  // from the row-major V tile through transposed reads (two per MFMA).
+  auto pv = [&](const char* Vt, int kb) __attribute__((always_inline)) {
+    const char* Vs = Vt + kb * 32 * ROWB;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const char* a0 = Vs + (i >> 2) * 16 * ROWB + voff[i & 3];
@@ -450,20 +457,22 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
   // Tiles whose 64 keys all precede L need no mask.
   const int nplain = p.L > kbeg ? min(ntiles, (p.L - kbeg) / KT) : 0;
 
-  // Sub-step over 32-key block (t, kb) with a successor block (tn, kb ^ 1): the
-  // successor's score MFMAs, this block's softmax and this block's P.V MFMAs form one
-  // scheduling region, so the compiler interleaves MFMAs with the softmax VALU work; then
-  // the successor is masked (if it reaches past the context) and the running maximum
-  // updated. The score buffer index equals kb.
-  auto sub = [&](int t, auto kbc, int tn) __attribute__((always_inline)) {
+  // Sub-step over 32-key block (t, kb) with a successor block (tn, kb ^ 1), whose K tile
+  // is at Kn (V of tile t at Vt): the successor's score MFMAs, this block's softmax and
+  // this block's P.V MFMAs form one scheduling region, so the compiler interleaves MFMAs
+  // with the softmax VALU work; then the successor is masked (if it reaches past the
+  // context) and the running maximum updated. The score buffer index equals kb.
+  auto sub = [&](int t, auto kbc, int tn, const char* Kn, const char* Vt) __attribute__((always_inline)) {
     constexpr int kb = decltype(kbc)::value;
     constexpr int kbn = kb ^ 1;
-    qk(tn, kbn, kbn);
+    qk(Kn, kbn, kbn);
     probs(kb);
-    pv(t, kb);
+    pv(Vt, kb);
     if (tn >= nplain) mask(kbeg + tn * KT + kbn * 32, kbn);
     rescale(kbn);
   };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
 
   // FP8: widen the K (or V) codes of raw tile t into its bf16 stage. Thread i converts
   // 16 codes (row i/8, dims 16*(i%8) ..) with the row's scale 2^e and writes the two bf16
@@ -474,7 +483,7 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
     const char* raw = smem + (t & (F8_NRAW - 1)) * F8_RAW_B + (is_v ? F8_TILE_B : 0);
     const int* ex = reinterpret_cast<const int*>(smem + (t & (F8_NRAW - 1)) * F8_RAW_B + 2 * F8_TILE_B) +
                     (is_v ? KT : 0);
-    char* dst = const_cast<char*>(is_v ? vstage(t) : kstage(t));
+    char* dst = const_cast<char*>(is_v ? vstage(t) + VBASE : kstage(t));
 #pragma unroll
     for (int pass = 0; pass < 8 / NW; ++pass) {
       const int idx = pass * NW * 64 + tid;
@@ -515,7 +524,7 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
       barrier_keep<DPT>();
     else
       barrier_keep<0>();
-    qk(0, 0, 0);
+    qk(kstage(0), 0, 0);
     if (nplain == 0) mask(kbeg, 0);
     rescale(0);
 
@@ -527,8 +536,8 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
       if (t + 4 < ntiles) issue(t + 4);
       if (t + 2 < ntiles) widen(t + 2, false);
       widen(t + 1, true);
-      sub(t, std::integral_constant<int, 0>{}, t);
-      sub(t, std::integral_constant<int, 1>{}, t + 1);
+      sub(t, B0{}, t, kstage(t), vstage(t));
+      sub(t, B1{}, t + 1, kstage(t + 1), vstage(t));
       if (t + 4 < ntiles)
         barrier_keep<DPT>();
       else
@@ -543,25 +552,44 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
     barrier_keep<DPT>();
   else
     barrier_keep<0>();
-  qk(0, 0, 0);
+  qk(kstage(0), 0, 0);
   if (nplain == 0) mask(kbeg, 0);
   rescale(0);
 
   // Tile t: block 0 (successor: block 1 of tile t), block 1 (successor: block 0 of tile
   // t+1); the barrier after each tile guarantees tile t+2 and keeps tile t+3 in flight.
   // Stage reuse: tile t+3 overwrites tile t-1, whose last reads were in tile t-1's blocks.
-  for (int t = 0; t + 1 < ntiles; ++t) {
+  // Unrolled by the ring length so that stage offsets are constants (folded into the
+  // ds_read offsets); the up to three steps left over use computed stages.
+  auto step = [&](int t, auto stc) __attribute__((always_inline)) {
+    constexpr int st = decltype(stc)::value;
     if (t + 3 < ntiles) issue(t + 3);
-    sub(t, std::integral_constant<int, 0>{}, t);
-    sub(t, std::integral_constant<int, 1>{}, t + 1);
+    const char* K0 = smem + st * TILE_B;
+    const char* K1 = smem + ((st + 1) & (NSTAGE - 1)) * TILE_B;
+    const char* V0 = smem + st * TILE_B;
+    sub(t, B0{}, t, K0, V0);
+    sub(t, B1{}, t + 1, K1, V0);
+    wait_step(t);
+  };
+  int t = 0;
+  for (; t + 4 < ntiles; t += 4) {
+    step(t, std::integral_constant<int, 0>{});
+    step(t + 1, std::integral_constant<int, 1>{});
+    step(t + 2, std::integral_constant<int, 2>{});
+    step(t + 3, std::integral_constant<int, 3>{});
+  }
+  for (; t + 1 < ntiles; ++t) {
+    if (t + 3 < ntiles) issue(t + 3);
+    sub(t, B0{}, t, kstage(t), vstage(t));
+    sub(t, B1{}, t + 1, kstage(t + 1), vstage(t));
     wait_step(t);
   }
   }
   {
     const int t = ntiles - 1;
-    sub(t, std::integral_constant<int, 0>{}, t);
+    sub(t, B0{}, t, kstage(t), vstage(t));
     probs(1);
-    pv(t, 1);
+    pv(vstage(t), 1);
   }
 
   // ---- partial result of this split

@@ -37,36 +37,49 @@ __device__ __forceinline__ uint32_t e4m3_rne(float y) {
   return code;
 }
 
-// One wave per (token, head) row of 128 values, two per lane.
+// 16 lanes per (token, head) row of 128 values, 8 per lane (one 16-byte load, one 8-byte
+// store); 16 rows per 256-thread block.
 __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __restrict__ src, int64_t st, int64_t sh,
                                                           int T, int H, uint8_t* __restrict__ codes, int64_t cst,
                                                           int64_t csh, int32_t* __restrict__ exps) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= T * H) return;
-  const int t = row / H, h = row % H;
-  const uint32_t w = *reinterpret_cast<const uint32_t*>(src + (int64_t)t * st + (int64_t)h * sh + 2 * lane);
-  const float x0 = bf16_lo(w), x1 = bf16_hi(w);
-  float amax = fmaxf(fabsf(x0), fabsf(x1));
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  if (row >= (int64_t)T * H) return;  // whole 16-lane groups leave together
+  const int64_t t = row / H;
+  const int h = (int)(row % H);
+  const u32x4 w = *reinterpret_cast<const u32x4*>(src + t * st + (int64_t)h * sh + 8 * sub);
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = bf16_lo(w[j]);
+    x[2 * j + 1] = bf16_hi(w[j]);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+  for (int off = 8; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   int e = 0;
   if (amax > 0.f) {
     int k;
     const float m = frexpf(amax, &k);  // amax = m * 2^k, m in [0.5, 1); 448 = 0.875 * 2^9
     e = m <= 0.875f ? k - 9 : k - 8;
   }
-  const uint32_t c0 = e4m3_rne(ldexpf(x0, -e));
-  const uint32_t c1 = e4m3_rne(ldexpf(x1, -e));
-  *reinterpret_cast<uint16_t*>(codes + (int64_t)t * cst + (int64_t)h * csh + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
-  if (lane == 0) exps[(int64_t)t * H + h] = e;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    lo |= e4m3_rne(ldexpf(x[j], -e)) << (8 * j);
+    hi |= e4m3_rne(ldexpf(x[4 + j], -e)) << (8 * j);
+  }
+  *reinterpret_cast<uint2*>(codes + t * cst + (int64_t)h * csh + 8 * sub) = make_uint2(lo, hi);
+  if (sub == 0) exps[row] = e;
 }
 
 }  // namespace
 
 hipError_t launch_kv_quantize(const void* src, int64_t st, int64_t sh, int T, int H, void* codes, int64_t cst,
                               int64_t csh, int32_t* exps, hipStream_t stream) {
-  const int rows = T * H;
-  hipLaunchKernelGGL(kv_quantize_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream,
+  const int64_t rows = (int64_t)T * H;
+  hipLaunchKernelGGL(kv_quantize_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(src), st, sh, T, H, static_cast<uint8_t*>(codes), cst, csh, exps);
   return hipGetLastError();
 }
