@@ -234,6 +234,10 @@ def test_binding_refuses_cpu_tensors():
     ((FAKE, 1022, 128, 10, 8, 128, FAKE, 1024, 128, FAKE), 1),
     ((FAKE, 1024, 126, 10, 8, 128, FAKE, 1024, 128, FAKE), 1),
     ((FAKE, 1024, 128, 10, 8, 128, FAKE, 1024, 127, FAKE), 1),
+    ((FAKE, 1028, 128, 10, 8, 128, FAKE, 1024, 128, FAKE), 1),
+    ((FAKE, 1024, 128, 10, 8, 128, FAKE, 1024, 132, FAKE), 1),
+    ((ctypes.c_void_p(0x10008), 1024, 128, 10, 8, 128, FAKE, 1024, 128, FAKE), 1),
+    ((FAKE, 1024, 128, 10, 8, 128, ctypes.c_void_p(0x10004), 1024, 128, FAKE), 1),
     ((FAKE, 1024, 128, 10, 8, 128, FAKE, 1023, 128, FAKE), 1),
     ((ctypes.c_void_p(0x10002), 1024, 128, 10, 8, 128, FAKE, 1024, 128, FAKE), 1),
     ((FAKE, 1024, 128, 10, 8, 128, ctypes.c_void_p(0x10001), 1024, 128, FAKE), 1),

@@ -492,22 +492,42 @@ def _sample_dev(logits_dev, parent, draft, T, seed, offset):
     return tok.cpu().numpy(), ln.item(), nodes.cpu().numpy(), toks.cpu().numpy(), bonus.item()
 
 
+def _check_sampled_tokens(x, T, seed, offset, tok):
+    """The kernel scores logit / T + Gumbel noise in float32; the oracle in float64. The
+    sampled token is unique unless a row's two best scores lie within the float32 error of
+    the kernel's score: fma rounding of x / T plus two hardware logarithms, bounded here by
+    2^-20 (1 + |x / T| + 17) per score (|G| <= 17 for the 23-bit uniforms). Tokens must
+    equal the oracle's, except on such near-tie rows, where the kernel's token must score
+    within twice that bound of the row maximum."""
+    u = oracle.uniforms(x.shape[0], x.shape[1], seed, offset)
+    sc = x / T - np.log(-np.log(u))
+    etok = sc.argmax(axis=1)
+    diff = np.flatnonzero(tok != etok)
+    for i in diff:
+        tol = 2 * 2.0 ** -20 * (1 + np.abs(x[i] / T).max() + 17)
+        assert sc[i, tok[i]] >= sc[i].max() - tol, (i, tok[i], etok[i])
+    assert len(diff) <= max(1, len(tok) // 50), diff
+    return etok
+
+
 @pytest.mark.parametrize("name,T,seed,offset", [("tiny_chain", 1.0, 7, 0), ("tiny_chain", 0.3, 7, 1),
                                                 ("budget22", 1.0, 123456789012, 5), ("budget22", 2.5, 3, 1 << 40),
                                                 ("decode_1node", 0.8, 42, 9)])
 def test_sample_accept_matches_oracle(name, T, seed, offset):
-    """Same Philox stream and Gumbel-max rule: the sampled tokens equal the oracle's
-    (a different choice would need the top two scores of a row within float32 rounding),
-    and the walk on them is bit exact."""
+    """Same Philox stream and Gumbel-max rule: the sampled tokens are the oracle's (up to
+    float32 near-ties, see _check_sampled_tokens), and the walk on them is bit exact."""
     w = make(name, 0, parts=("tree", "logits"))
     note(f"sample_accept {name} T={T}")
     if w.logits_dtype == "bf16":
         lg, x = dev_bf16(w.logits), oracle.bf16_bits_to_f64(w.logits)
     else:
         lg, x = torch.from_numpy(w.logits).cuda(), w.logits.astype(np.float64)
-    etok, (eln, enodes, etoks, ebonus) = oracle.sample_accept(w.parent, w.draft, x, T, seed, offset)
     tok, ln, nodes, toks, bonus = _sample_dev(lg, w.parent, w.draft, T, seed, offset)
-    assert np.array_equal(tok, etok)
+    etok = _check_sampled_tokens(x, T, seed, offset, tok)
+    if np.array_equal(tok, etok):
+        otok, _ = oracle.sample_accept(w.parent, w.draft, x, T, seed, offset)
+        assert np.array_equal(otok, etok)
+    eln, enodes, etoks, ebonus = oracle.accept(w.parent, w.draft, tok)
     assert ln == eln and nodes[:ln].tolist() == enodes.tolist() and toks[:ln].tolist() == etoks.tolist()
     assert (nodes[ln:] == -1).all() and bonus == ebonus
 
@@ -527,8 +547,8 @@ def test_sample_accept_layouts(dtype, V, stride):
     etok = oracle.sample_rows(xv, 1.3, 77, 3)
     draft = np.where(rng.random(n) < 0.6, etok, (etok + 1) % V).astype(np.int32)
     tok, ln, nodes, _, bonus = _sample_dev(lg, parent, draft, 1.3, 77, 3)
-    assert np.array_equal(tok, etok)
-    e_ln, e_nodes, _, e_bonus = oracle.accept(parent, draft, etok)
+    _check_sampled_tokens(xv, 1.3, 77, 3, tok)
+    e_ln, e_nodes, _, e_bonus = oracle.accept(parent, draft, tok)
     assert ln == e_ln and nodes[:ln].tolist() == e_nodes.tolist() and bonus == e_bonus
 
 
