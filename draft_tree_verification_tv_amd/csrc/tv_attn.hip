@@ -8,7 +8,11 @@
 // Design (split-KV flash decoding, MFMA form):
 //   * Rows. For KV head h the G = Hq/Hkv query heads of all N nodes are stacked into
 //     M = G*N rows (row r -> node r/G, q head h*G + r%G), so one K/V tile read from HBM
-//     is used by every row that needs it. A workgroup owns up to 256 rows, 32 per wave.
+//     is used by every row that needs it. A workgroup always runs 8 waves: RWV row-waves
+//     of 32 rows times KSW key-waves (8x1 for M > 128; 4x2, 2x4, 1x8 for fewer rows).
+//     Key-wave k takes every KSW-th 32-key block of the split with its own online
+//     softmax; the key-waves' partial results are merged in LDS at the end, so small
+//     trees and single-token decode still keep two waves busy on every SIMD.
 //   * Splits. The key sequence [0, L+N) is cut into S ranges; each workgroup streams one
 //     range for one (KV head, row tile) and writes a normalised fp32 partial output and
 //     its log2-sum-exp. attn_merge_kernel combines the partials.
@@ -168,8 +172,11 @@ __device__ __forceinline__ void barrier_keep(void) {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(kPending) : "memory");
 }
 
-template <int NW, bool kF8>
-__global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
+template <int RWV, int KSW, bool kF8>
+__global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams p) {
+  constexpr int NW = RWV * KSW;
+  constexpr int ROWS = RWV * 32;  // stacked rows per workgroup
+  static_assert(NW == 8, "eight waves per workgroup");
   // Copies per wave per tile: bf16, 16 blocks of 1 KB for each of K and V; FP8, 8 blocks
   // of codes for each plus one copy of 128 / NW exponents.
   constexpr int BLK = kF8 ? KT / 8 : KT / 4;
@@ -202,7 +209,9 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
   const int i16 = lane & 15;
   const int g16 = (lane >> 4) & 1;
 
-  const int r = rt * TILE_ROWS + wave * 32 + ql;
+  const int rw = wave % RWV;  // row-wave
+  const int kw = wave / RWV;  // key-wave
+  const int r = rt * ROWS + rw * 32 + ql;
   const bool rvalid = r < p.M;
   const int node = rvalid ? r / p.G : 0;
   const int qh = h * p.G + (rvalid ? r % p.G : 0);
@@ -358,14 +367,16 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
       return smem + (t & (NSTAGE - 1)) * TILE_B;
   };
 
-  // S^T of 32-key block kb of the K tile at Kt into sc[c]: 8 K fragments, 8 MFMAs.
-  auto qk = [&](const char* Kt, int kb, int c) __attribute__((always_inline)) {
+  // S^T of 32-key block kb of the K tile at Kt: 8 K fragments, 8 MFMAs.
+  auto qk_v = [&](const char* Kt, int kb) __attribute__((always_inline)) -> f32x16 {
     const char* Ks = Kt + kb * 32 * ROWB;
-    sc[c] = f32x16{};
+    f32x16 acc = f32x16{};
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8)
-      sc[c] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + koff[s8]), qf[s8], sc[c]);
+      acc = mfma32(*reinterpret_cast<const bf16x8*>(Ks + koff[s8]), qf[s8], acc);
+    return acc;
   };
+  auto qk = [&](const char* Kt, int kb, int c) __attribute__((always_inline)) { sc[c] = qk_v(Kt, kb); };
 
   // O^T += V^T P^T over 32-key block kb of the V tile at Vt + VBASE; V^T fragments come
   // from the row-major V tile through transposed reads (two per MFMA).
@@ -474,6 +485,48 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
 
+  // Key-waves (KSW > 1): this wave owns half kbw of every tile t with t % KP == kph.
+  // Its block's scores are computed one step ahead (tile t+1 has landed by then) into
+  // sc[0]; at its own step it forms the probabilities and the P.V product. With KP == 1
+  // both happen in every step, the next block's scores going to a temporary first so that
+  // its MFMAs can overlap this block's softmax.
+  constexpr int KP = KSW > 1 ? KSW / 2 : 1;
+  const int kph = kw % KP;
+  const int kbw = kw / KP;
+  auto key_step = [&](int t) __attribute__((always_inline)) {
+    if constexpr (KP == 1) {
+      if (t + 1 < ntiles) {
+        const f32x16 nx = qk_v(kstage(t + 1), kbw);
+        probs(0);
+        pv(vstage(t), kbw);
+        sc[0] = nx;
+        if (t + 1 >= nplain) mask(kbeg + (t + 1) * KT + kbw * 32, 0);
+        rescale(0);
+      } else {
+        probs(0);
+        pv(vstage(t), kbw);
+      }
+    } else {
+      if ((t & (KP - 1)) == kph) {
+        probs(0);
+        pv(vstage(t), kbw);
+      }
+      if (t + 1 < ntiles && ((t + 1) & (KP - 1)) == kph) {
+        qk(kstage(t + 1), kbw, 0);
+        if (t + 1 >= nplain) mask(kbeg + (t + 1) * KT + kbw * 32, 0);
+        rescale(0);
+      }
+    }
+  };
+  // First scores of a key-wave whose first block lies in tile 0 (tiles 0 and 1 landed).
+  auto key_prologue = [&]() __attribute__((always_inline)) {
+    if (kph == 0) {
+      qk(kstage(0), kbw, 0);
+      if (nplain == 0) mask(kbeg + kbw * 32, 0);
+      rescale(0);
+    }
+  };
+
   // FP8: widen the K (or V) codes of raw tile t into its bf16 stage. Thread i converts
   // 16 codes (row i/8, dims 16*(i%8) ..) with the row's scale 2^e and writes the two bf16
   // chunks to their swizzled places. Exponents outside [kExpMin, kExpMax] are clamped and
@@ -524,6 +577,21 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
       barrier_keep<DPT>();
     else
       barrier_keep<0>();
+    if constexpr (KSW > 1) {
+      key_prologue();
+      for (int t = 0; t < ntiles; ++t) {
+        if (t + 4 < ntiles) issue(t + 4);
+        if (t + 2 < ntiles) widen(t + 2, false);
+        if (t + 1 < ntiles) widen(t + 1, true);
+        key_step(t);
+        if (t + 1 < ntiles) {
+          if (t + 4 < ntiles)
+            barrier_keep<DPT>();
+          else
+            barrier_keep<0>();
+        }
+      }
+    } else {
     qk(kstage(0), 0, 0);
     if (nplain == 0) mask(kbeg, 0);
     rescale(0);
@@ -543,7 +611,28 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
       else
         barrier_keep<0>();
     }
+    {
+      const int t = ntiles - 1;
+      sub(t, B0{}, t, kstage(t), vstage(t));
+      probs(1);
+      pv(vstage(t), 1);
+    }
+    }
     if (__any(bad_exp) && lane == 0 && p.dev_error) *p.dev_error = TV_ERR_INVALID_ARG;
+  } else if constexpr (KSW > 1) {
+    // ---- key-waves: tiles 0, 1, 2 start streaming; tiles 0 and 1 must land.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    for (int t = 0; t < 3 && t < ntiles; ++t) issue(t);
+    if (ntiles > 2)
+      barrier_keep<DPT>();
+    else
+      barrier_keep<0>();
+    key_prologue();
+    for (int t = 0; t < ntiles; ++t) {
+      if (t + 3 < ntiles) issue(t + 3);
+      key_step(t);
+      if (t + 1 < ntiles) wait_step(t);
+    }
   } else {
   // ---- prologue: tiles 0, 1, 2 start streaming; tiles 0 and 1 must land.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // query loads are not tile copies
@@ -584,12 +673,49 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
     sub(t, B1{}, t + 1, kstage(t + 1), vstage(t));
     wait_step(t);
   }
-  }
   {
     const int t = ntiles - 1;
     sub(t, B0{}, t, kstage(t), vstage(t));
     probs(1);
     pv(vstage(t), 1);
+  }
+  }
+
+  // ---- key-waves: merge the KSW partial states of each row in LDS (the ring is free:
+  // every copy has landed and every wave has finished its reads at the barrier). Each
+  // key-wave k > 0 leaves O (64 values per lane, lane-interleaved), its reference maximum
+  // and its row-sum part; key-wave 0 rescales all to the common maximum and adds them.
+  if constexpr (KSW > 1) {
+    barrier_keep<0>();
+    constexpr int SLOT = 64 * 64 + 128;  // floats per (row-wave, key-wave)
+    float* ms = reinterpret_cast<float*>(smem);
+    if (kw > 0) {
+      float* b = ms + ((kw - 1) * RWV + rw) * SLOT;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) b[(db * 16 + i) * 64 + lane] = o[db][i];
+      b[4096 + lane] = m_ref;
+      b[4096 + 64 + lane] = lsum;
+    }
+    barrier_keep<0>();
+    if (kw == 0) {
+#pragma unroll 1
+      for (int k = 1; k < KSW; ++k) {
+        const float* b = ms + ((k - 1) * RWV + rw) * SLOT;
+        const float mk = b[4096 + lane];
+        const float lk = b[4096 + 64 + lane];
+        const float mn = fmaxf(m_ref, mk);
+        const float a0 = m_ref == -INFINITY ? 0.f : exp2f(m_ref - mn);
+        const float ak = mk == -INFINITY ? 0.f : exp2f(mk - mn);
+        lsum = lsum * a0 + lk * ak;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][i] = o[db][i] * a0 + b[(db * 16 + i) * 64 + lane] * ak;
+        m_ref = mn;
+      }
+    }
   }
 
   // ---- partial result of this split
@@ -599,8 +725,8 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(SplitParams p) {
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   const float lse2 = lsum > 0.f ? m_ref + __log2f(lsum) : -INFINITY;
-  if (rvalid) {
-    const int64_t base = ((int64_t)(h * p.RT + rt) * p.S + s) * TILE_ROWS + wave * 32 + ql;
+  if (rvalid && kw == 0) {
+    const int64_t base = ((int64_t)(h * p.RT + rt) * p.S + s) * TILE_ROWS + rw * 32 + ql;
     float* po = p.part_o + base * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -621,6 +747,7 @@ struct MergeParams {
   uint16_t* out;
   float* lse;
   int N, Hq, G, RT, S;
+  int rows;  // stacked rows per workgroup of the split kernel
 };
 
 // One wave per (node, q head) row, two head-dim values per lane:
@@ -634,8 +761,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams mp) {
   const int qh = row % mp.Hq;
   const int h = qh / mp.G;
   const int r = n * mp.G + qh % mp.G;
-  const int rt = r / TILE_ROWS;
-  const int64_t base0 = (int64_t)(h * mp.RT + rt) * mp.S * TILE_ROWS + (r % TILE_ROWS);
+  const int rt = r / mp.rows;
+  const int64_t base0 = (int64_t)(h * mp.RT + rt) * mp.S * TILE_ROWS + (r % mp.rows);
   const float* lse_p = mp.part_lse + base0;
   const float* o_p = mp.part_o + base0 * D + 2 * lane;
 
@@ -674,17 +801,18 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams mp) {
   if (mp.lse && lane == 0) mp.lse[row] = mx == -INFINITY ? -INFINITY : (mx + __log2f(wsum)) * kLn2;
 }
 
-template <int NW, bool kF8>
+template <int RWV, bool kF8>
 hipError_t launch_split(const SplitParams& sp, int nwg, hipStream_t stream) {
+  constexpr int KSW = 8 / RWV;
   constexpr int smem = kF8 ? F8_SMEM_BYTES : SMEM_BYTES;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_split_kernel<NW, kF8>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_split_kernel<RWV, KSW, kF8>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((attn_split_kernel<NW, kF8>), dim3(nwg), dim3(NW * 64), smem, stream, sp);
+  hipLaunchKernelGGL((attn_split_kernel<RWV, KSW, kF8>), dim3(nwg), dim3(512), smem, stream, sp);
   return hipGetLastError();
 }
 
@@ -694,9 +822,11 @@ AttnPlan attn_plan(int N, int L, int Hq, int Hkv, int num_splits, int num_cus) {
   AttnPlan p;
   p.G = Hq / Hkv;
   p.M = p.G * N;
-  p.RT = (p.M + TILE_ROWS - 1) / TILE_ROWS;
+  // Row-waves: the power of two of 32-row waves that covers min(M, 256) rows; the rest of
+  // the eight waves split the keys.
   const int rows = p.M < TILE_ROWS ? p.M : TILE_ROWS;
-  p.NW = rows <= 64 ? 2 : rows <= 128 ? 4 : 8;
+  p.RWV = rows <= 32 ? 1 : rows <= 64 ? 2 : rows <= 128 ? 4 : 8;
+  p.RT = (p.M + p.RWV * 32 - 1) / (p.RWV * 32);
   p.T = L + N;
   const int tiles = (p.T + KT - 1) / KT;
   int S = num_splits;
@@ -763,13 +893,15 @@ hipError_t launch_attn(const AttnPlan& plan, bool f8, const void* q, const void*
 
   hipError_t e;
   if (f8) {
-    switch (plan.NW) {
+    switch (plan.RWV) {
+      case 1: e = launch_split<1, true>(sp, nwg, stream); break;
       case 2: e = launch_split<2, true>(sp, nwg, stream); break;
       case 4: e = launch_split<4, true>(sp, nwg, stream); break;
       default: e = launch_split<8, true>(sp, nwg, stream); break;
     }
   } else {
-    switch (plan.NW) {
+    switch (plan.RWV) {
+      case 1: e = launch_split<1, false>(sp, nwg, stream); break;
       case 2: e = launch_split<2, false>(sp, nwg, stream); break;
       case 4: e = launch_split<4, false>(sp, nwg, stream); break;
       default: e = launch_split<8, false>(sp, nwg, stream); break;
@@ -787,6 +919,7 @@ hipError_t launch_attn(const AttnPlan& plan, bool f8, const void* q, const void*
   mp.G = plan.G;
   mp.RT = plan.RT;
   mp.S = plan.S;
+  mp.rows = plan.RWV * 32;
   const int rows_out = N * Hq;
   hipLaunchKernelGGL(attn_merge_kernel, dim3((rows_out + 3) / 4), dim3(256), 0, stream, mp);
   return hipGetLastError();

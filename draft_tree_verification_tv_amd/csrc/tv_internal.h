@@ -188,8 +188,8 @@ hipError_t launch_argmax_accept(const void* logits, int dtype, int N, int V, int
 
 struct AttnPlan {
   int G, M;        // q heads per KV head; stacked rows per KV head (G * N)
-  int RT;          // row tiles of up to 256 stacked rows
-  int NW;          // waves per workgroup: 2, 4 or 8 (32 rows each)
+  int RT;          // row tiles of RWV * 32 stacked rows
+  int RWV;         // row-waves per workgroup (1, 2, 4 or 8); the other 8 / RWV split keys
   int S;           // KV splits actually launched
   int KS;          // keys per split (multiple of the key tile)
   int T;           // L + N
