@@ -752,6 +752,9 @@ struct MergeParams {
 
 // One wave per (node, q head) row, two head-dim values per lane:
 // lse = M + log2 sum_s 2^(lse_s - M), out = sum_s 2^(lse_s - lse) * out_s.
+// Lane s of a 64-split chunk holds split s's weight; the partial outputs are read in
+// batches of 16 independent loads (addresses clamped into the chunk, weight 0 past its
+// end), so a row costs a few memory round trips whatever the split count.
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams mp) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -773,27 +776,25 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams mp) {
   f32x2 acc = {0.f, 0.f};
   float wsum = 0.f;
   if (mx != -INFINITY) {
-    int s = 0;
-    for (; s + 8 <= mp.S; s += 8) {
-      float l8[8];
-      f32x2 x8[8];
+    for (int s0 = 0; s0 < mp.S; s0 += 64) {
+      const int cnt = min(64, mp.S - s0);
+      const float w = lane < cnt ? exp2f(lse_p[(int64_t)(s0 + lane) * TILE_ROWS] - mx) : 0.f;
+      wsum += w;
+      for (int j = 0; j < cnt; j += 16) {
+        f32x2 x[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        l8[u] = lse_p[(int64_t)(s + u) * TILE_ROWS];
-        x8[u] = *reinterpret_cast<const f32x2*>(o_p + (int64_t)(s + u) * TILE_ROWS * D);
-      }
+        for (int u = 0; u < 16; ++u) {
+          const int sj = s0 + min(j + u, cnt - 1);
+          x[u] = *reinterpret_cast<const f32x2*>(o_p + (int64_t)sj * TILE_ROWS * D);
+        }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float wgt = exp2f(l8[u] - mx);
-        wsum += wgt;
-        acc += wgt * x8[u];
+        for (int u = 0; u < 16; ++u) {
+          const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j + u));
+          acc += (j + u < cnt ? wu : 0.f) * x[u];
+        }
       }
     }
-    for (; s < mp.S; ++s) {
-      const float wgt = exp2f(lse_p[(int64_t)s * TILE_ROWS] - mx);
-      wsum += wgt;
-      acc += wgt * *reinterpret_cast<const f32x2*>(o_p + (int64_t)s * TILE_ROWS * D);
-    }
+    for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const bf16x2 ob = __builtin_convertvector((f32x2{acc[0] * inv, acc[1] * inv}), bf16x2);
