@@ -35,10 +35,10 @@ CPU_SAMPLE_SECONDS = 10.0
 # copy (read factor 2.0, write factor 1.0); summary in
 # profiles/tv_tree_attn_long_128k_hbm_counters.md. Valid only for the kernel sources they
 # were taken on: reported as null once those sources change.
-TRAFFIC_BYTES_PER_CALL = 610458196
+TRAFFIC_BYTES_PER_CALL = 607869733
 TRAFFIC_SOURCES = ("draft_tree_verification_tv_amd/csrc/tv_attn.hip",
                    "draft_tree_verification_tv_amd/csrc/tv_internal.h")
-TRAFFIC_SOURCES_SHA256 = "1666db9ae5fb5f5ad602bf475b7db798d52214ec3050ea2a22e32c25e3d46cfd"
+TRAFFIC_SOURCES_SHA256 = "9b1a58d1cde696fcaf4d39a3f9aa5cb8fabe0a3cb27c854b299166ff6750f167"
 
 
 def measured_traffic():
