@@ -235,10 +235,10 @@ int tv_kv_commit(void* k, void* v, int64_t kv_stride_t, int64_t kv_stride_h, int
  * (bias 7, no infinities, largest finite 448) nearest to x * 2^-e, ties to the even
  * mantissa, -0 coded as +0. The row dequantises to decode(code) * 2^e, which is exact in
  * bfloat16.
- *   src          bf16 [T][Hkv][D], strides src_stride_t / src_stride_h in elements (even),
- *                D contiguous; 4-byte aligned. Values must be finite.
+ *   src          bf16 [T][Hkv][D], strides src_stride_t / src_stride_h in elements
+ *                (multiples of 8), D contiguous; 16-byte aligned. Values must be finite.
  *   codes        uint8 [T][Hkv][D] out, strides codes_stride_t / codes_stride_h in bytes
- *                (even), D contiguous; 2-byte aligned.
+ *                (multiples of 8), D contiguous; 8-byte aligned.
  *   exps         int32 [T * Hkv] out (row t * Hkv + h), 4-byte aligned.
  * Limits: T >= 0 (T = 0 enqueues nothing), Hkv >= 1, D = TV_HEAD_DIM (else
  * TV_ERR_UNSUPPORTED), strides at least the packed ones.
