@@ -88,7 +88,7 @@ constexpr int kExpMin = -117;
 constexpr int kExpMax = 119;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleTh = 8.0f;
+constexpr float kCheck = 256.0f;  // largest probability (and 16-key partial sum) kept
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -416,33 +416,12 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
     }
   };
 
-  // Lazy online-softmax rescale to the maximum of block sc[c]: the reference maximum moves
-  // only when a block exceeds it by more than 2^8. A row's 32 keys are split between lanes
-  // l and l ^ 32, whose maxima permlane32_swap exchanges (max(r0, r1) is the row maximum
-  // in both).
-  auto rescale = [&](int c) __attribute__((always_inline)) {
-    // One v_max3 per two new scores (8 instructions for 16).
-    float m = fmaxf(fmaxf(sc[c][0], sc[c][1]), sc[c][2]);
-#pragma unroll
-    for (int e = 3; e < 15; e += 2) m = fmaxf(fmaxf(m, sc[c][e]), sc[c][e + 1]);
-    m = fmaxf(m, sc[c][15]);
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-    const float mt = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])) * p.c;
-    const bool need = mt > m_ref + kRescaleTh;
-    if (__any(need)) {
-      const float m_new = need ? mt : m_ref;
-      const float alpha = need ? exp2f(m_ref - m_new) : 1.f;
-      lsum *= alpha;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] *= alpha;
-      m_ref = m_new;
-    }
-  };
-
-  // Probabilities of block sc[c] relative to m_ref: unrounded fp32 row sums, bf16 P^T
-  // fragments for the P.V MFMAs.
-  auto probs = [&](int c) __attribute__((always_inline)) {
+  // Probabilities of block sc[c] relative to the reference m_ref (0 while it is unset):
+  // bf16 P^T fragments for the P.V MFMAs; returns this lane's unrounded fp32 sum of its
+  // 16 probabilities.
+  auto probs = [&](int c) __attribute__((always_inline)) -> float {
     const float mu = m_ref == -INFINITY ? 0.f : m_ref;
+    float bs = 0.f;
 #pragma unroll
     for (int th = 0; th < 2; ++th) {
       bf16x2 b[4];
@@ -451,10 +430,42 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[c][th * 8 + 2 * j], p.c, -mu));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[c][th * 8 + 2 * j + 1], p.c, -mu));
         b[j] = __builtin_convertvector((f32x2{p0, p1}), bf16x2);
-        lsum += p0 + p1;
+        bs += p0 + p1;
       }
       pb[th] = bf16x8{b[0][0], b[0][1], b[1][0], b[1][1], b[2][0], b[2][1], b[3][0], b[3][1]};
     }
+    return bs;
+  };
+
+  // Online softmax of block sc[c] with a lazy reference maximum. The probabilities are
+  // formed against the current reference first; the block needs a new reference only if
+  // one of them exceeds 2^8, and then its lane's partial sum does too. So only when some
+  // lane's sum exceeds 2^8 (or is infinite), or the reference is still unset, does the
+  // wave take the exact path: the row maximum (lanes l and l ^ 32 hold a row's 32 keys
+  // and exchange maxima through permlane32_swap), the reference raised to it, the row sum
+  // and O (which holds the earlier blocks) rescaled, the probabilities formed again.
+  // Probabilities therefore stay below 2^8 and the reference within 8 of the maximum;
+  // the common path needs no maximum at all.
+  auto softmax = [&](int c) __attribute__((always_inline)) {
+    float bs = probs(c);
+    const bool need = m_ref == -INFINITY || bs > kCheck;
+    if (__any(need)) {
+      // One v_max3 per two scores (8 instructions for 16).
+      float m = fmaxf(fmaxf(sc[c][0], sc[c][1]), sc[c][2]);
+#pragma unroll
+      for (int e = 3; e < 15; e += 2) m = fmaxf(fmaxf(m, sc[c][e]), sc[c][e + 1]);
+      m = fmaxf(m, sc[c][15]);
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+      const float mt = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])) * p.c;
+      const float m_new = fmaxf(m_ref, mt);
+      const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new);
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] *= alpha;
+      m_ref = m_new;
+      bs = probs(c);
+    }
+    lsum += bs;
   };
 
   // Barrier closing tile t: tile t+2 has landed; tile t+3 (if any) stays in flight.
@@ -477,10 +488,9 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
     constexpr int kb = decltype(kbc)::value;
     constexpr int kbn = kb ^ 1;
     qk(Kn, kbn, kbn);
-    probs(kb);
+    softmax(kb);
     pv(Vt, kb);
     if (tn >= nplain) mask(kbeg + tn * KT + kbn * 32, kbn);
-    rescale(kbn);
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
@@ -497,24 +507,22 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
     if constexpr (KP == 1) {
       if (t + 1 < ntiles) {
         const f32x16 nx = qk_v(kstage(t + 1), kbw);
-        probs(0);
+        softmax(0);
         pv(vstage(t), kbw);
         sc[0] = nx;
         if (t + 1 >= nplain) mask(kbeg + (t + 1) * KT + kbw * 32, 0);
-        rescale(0);
       } else {
-        probs(0);
+        softmax(0);
         pv(vstage(t), kbw);
       }
     } else {
       if ((t & (KP - 1)) == kph) {
-        probs(0);
+        softmax(0);
         pv(vstage(t), kbw);
       }
       if (t + 1 < ntiles && ((t + 1) & (KP - 1)) == kph) {
         qk(kstage(t + 1), kbw, 0);
         if (t + 1 >= nplain) mask(kbeg + (t + 1) * KT + kbw * 32, 0);
-        rescale(0);
       }
     }
   };
@@ -523,7 +531,6 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
     if (kph == 0) {
       qk(kstage(0), kbw, 0);
       if (nplain == 0) mask(kbeg + kbw * 32, 0);
-      rescale(0);
     }
   };
 
@@ -594,7 +601,6 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
     } else {
     qk(kstage(0), 0, 0);
     if (nplain == 0) mask(kbeg, 0);
-    rescale(0);
 
     // Step t: raw tile t+4 starts (into the stage of raw tile t, fully widened by step
     // t-1); K of tile t+2 and V of tile t+1 are widened (their raw tiles landed by the
@@ -614,7 +620,7 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
     {
       const int t = ntiles - 1;
       sub(t, B0{}, t, kstage(t), vstage(t));
-      probs(1);
+      softmax(1);
       pv(vstage(t), 1);
     }
     }
@@ -643,7 +649,6 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
     barrier_keep<0>();
   qk(kstage(0), 0, 0);
   if (nplain == 0) mask(kbeg, 0);
-  rescale(0);
 
   // Tile t: block 0 (successor: block 1 of tile t), block 1 (successor: block 0 of tile
   // t+1); the barrier after each tile guarantees tile t+2 and keeps tile t+3 in flight.
@@ -676,7 +681,7 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
   {
     const int t = ntiles - 1;
     sub(t, B0{}, t, kstage(t), vstage(t));
-    probs(1);
+    softmax(1);
     pv(vstage(t), 1);
   }
   }
