@@ -5,8 +5,7 @@
 // codes (bias 7, largest finite 448, subnormals at exponent 0) with one power-of-two
 // scale 2^e per (token, KV head) row, e the smallest exponent with max|x| <= 448 * 2^e.
 // Every step is exact except the intended rounding: x * 2^-e (ldexp), then
-// round-to-nearest-even onto the E4M3 grid (rintf on the value scaled to its binade's
-// integer grid). Dequantised values code * 2^e are exact in bfloat16, which is what the
+// round-to-nearest-even onto the E4M3 grid by the hardware conversion. Dequantised values code * 2^e are exact in bfloat16, which is what the
 // FP8 attention path feeds to its MFMAs.
 #include <cmath>
 
@@ -16,25 +15,16 @@ namespace tv {
 
 namespace {
 
-// E4M3 code of y, |y| <= 448: nearest code value, ties to the even mantissa.
-__device__ __forceinline__ uint32_t e4m3_rne(float y) {
-  const float a = fabsf(y);
-  uint32_t code;
-  if (a < 0x1p-6f) {
-    code = (uint32_t)rintf(a * 0x1p9f);  // subnormal grid 2^-9; 8 is the smallest normal
-  } else {
-    int k;
-    (void)frexpf(a, &k);                   // a in [2^(k-1), 2^k)
-    int E = k - 1;
-    uint32_t n = (uint32_t)rintf(ldexpf(a, 3 - E));  // in [8, 16]
-    if (n == 16) {
-      E += 1;
-      n = 8;
-    }
-    code = ((uint32_t)(E + 7) << 3) | (n - 8);
-  }
-  if (y < 0.f && code) code |= 0x80u;
-  return code;
+// E4M3 codes of four values with |y| <= 448, packed little-endian: the hardware
+// conversion (OCP E4M3, round to nearest even), then the sign bit cleared on zero codes
+// (a negative value that rounds to zero is coded +0). Byte trick: for a 7-bit magnitude
+// m, bit 7 of (m + 0x7F) | m is set iff m != 0, and no carry crosses a byte.
+__device__ __forceinline__ uint32_t e4m3_pack4(float y0, float y1, float y2, float y3) {
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, w, true);
+  const uint32_t mag = w & 0x7F7F7F7Fu;
+  const uint32_t nz = ((mag + 0x7F7F7F7Fu) | mag) & 0x80808080u;
+  return w & (nz | 0x7F7F7F7Fu);
 }
 
 // 16 lanes per (token, head) row of 128 values, 8 per lane (one 16-byte load, one 8-byte
@@ -64,12 +54,11 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __rest
     const float m = frexpf(amax, &k);  // amax = m * 2^k, m in [0.5, 1); 448 = 0.875 * 2^9
     e = m <= 0.875f ? k - 9 : k - 8;
   }
-  uint32_t lo = 0, hi = 0;
+  float y[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    lo |= e4m3_rne(ldexpf(x[j], -e)) << (8 * j);
-    hi |= e4m3_rne(ldexpf(x[4 + j], -e)) << (8 * j);
-  }
+  for (int j = 0; j < 8; ++j) y[j] = ldexpf(x[j], -e);  // exact: a power-of-two scaling
+  const uint32_t lo = e4m3_pack4(y[0], y[1], y[2], y[3]);
+  const uint32_t hi = e4m3_pack4(y[4], y[5], y[6], y[7]);
   *reinterpret_cast<uint2*>(codes + t * cst + (int64_t)h * csh + 8 * sub) = make_uint2(lo, hi);
   if (sub == 0) exps[row] = e;
 }
