@@ -35,10 +35,10 @@ CPU_SAMPLE_SECONDS = 10.0
 # copy (read factor 2.0, write factor 1.0); summary in
 # profiles/tv_tree_attn_long_128k_hbm_counters.md. Valid only for the kernel sources they
 # were taken on: reported as null once those sources change.
-TRAFFIC_BYTES_PER_CALL = 607869733
+TRAFFIC_BYTES_PER_CALL = 608159372
 TRAFFIC_SOURCES = ("draft_tree_verification_tv_amd/csrc/tv_attn.hip",
                    "draft_tree_verification_tv_amd/csrc/tv_internal.h")
-TRAFFIC_SOURCES_SHA256 = "9b1a58d1cde696fcaf4d39a3f9aa5cb8fabe0a3cb27c854b299166ff6750f167"
+TRAFFIC_SOURCES_SHA256 = "3099fbc200e95fb26576f29eadd53df7ff41c9f7d1080931cebe1deb0c0a68c2"
 
 
 def measured_traffic():
