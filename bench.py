@@ -205,6 +205,24 @@ def main():
     fp8_us = timed(fp8_call, reps=8 * nf8)
     del f8
 
+    # Streaming reference on this machine: a plain 1 GiB device-to-device copy (read and
+    # write counted), the best of five; context for the roofline fraction.
+    cp_n = 1 << 30
+    cp_src = torch.empty(cp_n, dtype=torch.uint8, device=dev).fill_(3)
+    cp_dst = torch.empty_like(cp_src)
+    cp_dst.copy_(cp_src)
+    torch.cuda.synchronize()
+    cp_best = float("inf")
+    for _ in range(5):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        cp_dst.copy_(cp_src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cp_best = min(cp_best, c0.elapsed_time(c1) * 1e-3)
+    copy_gbps = 2 * cp_n / cp_best / 1e9
+    del cp_src, cp_dst
+
     attn_ms = np.array([e[0].elapsed_time(e[1]) for e in events]) / layers
     tokens_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
     t_attn_us = float(np.median(attn_ms) * 1e3)
@@ -269,7 +287,20 @@ def main():
                 break
         cpu_us = (time.perf_counter() - t0) / reps * 1e6
         del qf, kf, vf, lf
+        cpu_model = "unknown"
+        try:
+            with open("/proc/cpuinfo") as f:
+                cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu_model)
+        except OSError:
+            pass
+        try:
+            from threadpoolctl import threadpool_info
+            blas_threads = max((d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"),
+                               default=None)
+        except Exception:  # threadpoolctl missing or unable to inspect the BLAS
+            blas_threads = None
         cpu = {"value": round(cpu_us, 1), "unit": "us per tree-verify call", "cores": threads, "kind": "oracle",
+               "cpu_model": cpu_model, "blas_threads": blas_threads,
                "sample": f"float64 numpy oracle on KV buffer 0 of the same workload: {reps} whole verify "
                          f"call(s) (tree attention of {N} nodes x {Hq} q heads over {T} keys, argmax of the "
                          f"[{N}, {V}] logits, accept walk), mean time per call; bf16->float64 input "
@@ -302,6 +333,7 @@ def main():
                          "tree_attn_fp8": round(fp8_us, 2), "kv_quantize_fp8_one_tensor": round(quant_us, 2)},
         "kv_gbps": round(kv_gbps, 1),
         "kv_hbm_frac": round(kv_gbps / HBM_PEAK_GBS, 4),
+        "hbm_copy_gbps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "tv_tree_attn (split + merge)", "algorithmic_bytes": algo_bytes,
