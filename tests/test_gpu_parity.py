@@ -588,3 +588,36 @@ def test_sample_low_temperature_is_greedy_and_repeatable():
     b = _sample_dev(lg, w.parent, w.draft, 1.0, 5, 0)[0]
     c = _sample_dev(lg, w.parent, w.draft, 1.0, 5, 1)[0]
     assert np.array_equal(a, b) and not np.array_equal(a, c)
+
+
+def test_one_workspace_serves_any_sequence_of_calls():
+    """One argmax workspace, sized for the largest call, reused by tv_argmax,
+    tv_argmax_accept and tv_sample_accept calls of varying shapes: every result still
+    matches the oracle (no call depends on what an earlier one left in it)."""
+    rng = np.random.default_rng(31)
+    Nmax, Vmax = 256, 20000
+    ws = tv.argmax_workspace(Nmax, Vmax, "cuda")
+    for case in range(24):
+        n = int(rng.integers(1, Nmax + 1))
+        V = int(rng.integers(1, Vmax + 1))
+        parent = random_tree_parent(rng, n, 16, 4) if n > 1 else np.array([-1], np.int32)
+        x = rng.standard_normal((n, V)).astype(np.float32)
+        etok = oracle.argmax_rows(x.astype(np.float64))
+        draft = np.where(rng.random(n) < 0.7, etok, (etok + 1) % V).astype(np.int32)
+        lg = torch.from_numpy(x).cuda()
+        note(f"workspace reuse case {case}: N={n} V={V}")
+        if case % 3 == 2:
+            t = tv.argmax(lg, workspace=ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(t.cpu().numpy(), etok)
+        if case % 4 == 3:
+            tok, (ln, nodes, _, bonus) = tv.sample_accept(lg, dev_i32(parent), dev_i32(draft), 0.7, 9, case,
+                                                          workspace=ws)
+        else:
+            tok, (ln, nodes, _, bonus) = tv.argmax_accept(lg, dev_i32(parent), dev_i32(draft), workspace=ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(tok.cpu().numpy(), etok), case
+        torch.cuda.synchronize()
+        tk = tok.cpu().numpy()
+        eln, enodes, _, ebonus = oracle.accept(parent, draft, tk)
+        assert ln.item() == eln and nodes.cpu().numpy()[:eln].tolist() == enodes.tolist() and bonus.item() == ebonus
