@@ -290,8 +290,9 @@ __global__ __launch_bounds__(kBlock) void sample_partial(const char* __restrict_
 }
 
 // One workgroup finishes the verify step: thread i reduces node row i's slice results to
-// the row argmax (loads batched eight slices at a time, indices clamped so that no load is
-// conditional; a repeated (value, index) pair cannot change the result), keeps the tokens
+// the row argmax (loads batched 32 slices at a time, one round trip for vocabularies up to
+// 262144 bf16 entries; indices clamped so that no load is conditional, and a repeated
+// (value, index) pair cannot change the result), keeps the tokens
 // in LDS and runs the acceptance walk on them (the walk of tv_accept). The tree
 // preprocessing and the draft loads are issued first so that their latency overlaps the
 // reduction. With a single slice per row the slice kernel already wrote tok.
@@ -318,17 +319,17 @@ __global__ __launch_bounds__(kFuseThreads) void argmax_accept_kernel(
       const float* pv = part_v + (int64_t)i * chunks;
       const int* pi = part_i + (int64_t)i * chunks;
       Best b{-INFINITY, INT_MAX};
-      for (int j0 = 0; j0 < chunks; j0 += 8) {
-        float v[8];
-        int ix[8];
+      for (int j0 = 0; j0 < chunks; j0 += 32) {
+        float v[32];
+        int ix[32];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 32; ++u) {
           const int j = min(j0 + u, chunks - 1);
           v[u] = pv[j];
           ix[u] = pi[j];
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) b = better(b, Best{v[u], ix[u]});
+        for (int u = 0; u < 32; ++u) b = better(b, Best{v[u], ix[u]});
       }
       t = b.i == INT_MAX ? -1 : b.i;
       tok[i] = t;
