@@ -22,6 +22,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -34,21 +35,29 @@ CPU_SAMPLE_SECONDS = 10.0
 # rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE), each calibrated against a 1 GiB device
 # copy (read factor 2.0, write factor 1.0); summary in
 # profiles/tv_tree_attn_long_128k_hbm_counters.md. Valid only for the kernel sources they
-# were taken on: reported as null once those sources change.
+# were taken on (compared through a digest of their code without comments): reported as
+# null once that code changes.
 TRAFFIC_BYTES_PER_CALL = 608159372
 TRAFFIC_SOURCES = ("draft_tree_verification_tv_amd/csrc/tv_attn.hip",
                    "draft_tree_verification_tv_amd/csrc/tv_internal.h")
-TRAFFIC_SOURCES_SHA256 = "3099fbc200e95fb26576f29eadd53df7ff41c9f7d1080931cebe1deb0c0a68c2"
+TRAFFIC_SOURCES_SHA256 = "4b38ebbb402a6953e14c2f276d4aabd7c0ae04d0b47b19296959b7342659344b"
+
+
+def code_digest(root, files):
+    """SHA-256 of the sources' code with // comments and blank space removed, so that a
+    comment edit does not void counters taken on unchanged code."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(root, f)) as fh:
+            text = re.sub(r"//[^\n]*", "", fh.read())
+        h.update("".join(text.split()).encode())
+    return h.hexdigest()
 
 
 def measured_traffic():
-    import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
-    h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
-        with open(os.path.join(root, f), "rb") as fh:
-            h.update(fh.read())
-    return TRAFFIC_BYTES_PER_CALL if h.hexdigest() == TRAFFIC_SOURCES_SHA256 else None
+    return TRAFFIC_BYTES_PER_CALL if code_digest(root, TRAFFIC_SOURCES) == TRAFFIC_SOURCES_SHA256 else None
 
 
 def parse():

@@ -33,12 +33,13 @@
 //     into probabilities it already issues the score MFMAs of block j+1 (into the other of
 //     two score buffers), then block j's P.V MFMAs: MFMA and VALU work of one wave overlap,
 //     and the two waves sharing a SIMD fill each other's stalls.
-//   * Softmax. exp2 with the scale folded into one FMA. The reference maximum is raised
-//     only when a block exceeds it by more than 2^8 (lazy rescaling), so the 64-register
-//     rescale of O is off the common path. Row sums use the unrounded fp32 probabilities
-//     (so the exported log-sum-exp is exact to fp32); P is rounded to bf16 only as the
-//     MFMA operand. The two lanes holding a row exchange maxima and sums with
-//     permlane32_swap.
+//   * Softmax. exp2 with the scale folded into one FMA, against a lazy reference maximum
+//     that moves only when a block would exceed it by more than 2^8; whether it must is
+//     read off the probabilities themselves (a lane's sum of 16 above 2^8), so the block
+//     maximum and the 64-register rescale of O are off the common path. Row sums use the
+//     unrounded fp32 probabilities (so the exported log-sum-exp is exact to fp32); P is
+//     rounded to bf16 only as the MFMA operand. The two lanes holding a row exchange
+//     maxima and sums with permlane32_swap.
 //   * Tree keys (rows L..L+N-1) are masked with per-node ancestor bitmasks built in LDS by
 //     the workgroups whose range reaches them.
 //   * Work items are remapped so that consecutive ones (the splits of one KV head) land
