@@ -128,17 +128,18 @@ def main():
 
     def step(ev=None):
         # Kernels go to the current stream: `stream` when eager, the capture stream while a
-        # graph is being recorded.
+        # graph is being recorded. ev[b] .. ev[b+1] brackets attention call b; the last pair
+        # brackets argmax + accept.
         if ev:
             ev[0].record(stream)
         for b in range(layers):
             tv.tree_attn(q, K[b], Vc[b], parent, L=L, scale=w.scale, num_splits=args.splits, out=out, workspace=ws)
-        if ev:
-            ev[1].record(stream)
+            if ev:
+                ev[b + 1].record(stream)
         # argmax over the vocabulary and the accept walk: one call, two launches
         tv.argmax_accept(logits, parent, draft, tok=tok, out=acc, workspace=am_ws)
         if ev:
-            ev[2].record(stream)
+            ev[layers + 1].record(stream)
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
@@ -155,7 +156,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(layers + 2)] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -232,9 +233,11 @@ def main():
     copy_gbps = 2 * cp_n / cp_best / 1e9
     del cp_src, cp_dst
 
-    attn_ms = np.array([e[0].elapsed_time(e[1]) for e in events]) / layers
-    tokens_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    # Every attention call timed on its own (steps x layers repetitions): median, p10, p90.
+    attn_ms = np.array([e[b].elapsed_time(e[b + 1]) for e in events for b in range(layers)])
+    tokens_ms = np.array([e[layers].elapsed_time(e[layers + 1]) for e in events])
     t_attn_us = float(np.median(attn_ms) * 1e3)
+    t_attn_mean_us = float(np.mean(attn_ms) * 1e3)  # the roofline uses the average duration
     t_tokens_us = float(np.median(tokens_ms) * 1e3)
     call_us = t_attn_us + t_tokens_us
     ms_per_step = wall * 1e3 / args.steps
@@ -242,7 +245,7 @@ def main():
     kv_bytes = 2 * T * Hkv * D * 2
     qo_bytes = 2 * N * Hq * D * 2
     algo_bytes = kv_bytes + qo_bytes
-    achieved = algo_bytes / (t_attn_us * 1e-6) / 1e9
+    achieved = algo_bytes / (t_attn_mean_us * 1e-6) / 1e9
     kv_gbps = kv_bytes / (t_attn_us * 1e-6) / 1e9
     log(f"attn {t_attn_us:.1f} us/call ({kv_gbps:.0f} GB/s KV, {kv_gbps / HBM_PEAK_GBS:.1%} of peak), "
         f"argmax+accept {t_tokens_us:.1f} us, step {ms_per_step:.2f} ms (graph replay {graph_ms_per_step:.2f} ms)")
@@ -334,7 +337,8 @@ def main():
                                "KV buffers + argmax + accept per step",
                    "kv_len": L, "nodes": N, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "vocab": V,
                    "layers_per_step": layers, "parallelism": "none (1 GPU)"},
-        "breakdown_us": {"attn_per_call": round(t_attn_us, 2), "argmax_accept": round(t_tokens_us, 2),
+        "breakdown_us": {"attn_per_call": round(t_attn_us, 2), "attn_mean": round(t_attn_mean_us, 2),
+                         "attn_calls_timed": int(attn_ms.size), "argmax_accept": round(t_tokens_us, 2),
                          "attn_p10": round(float(np.percentile(attn_ms, 10) * 1e3), 2),
                          "attn_p90": round(float(np.percentile(attn_ms, 90) * 1e3), 2)},
         "graph_ms_per_step": round(graph_ms_per_step, 3),
