@@ -13,7 +13,14 @@ the kernels run on). ``roofline`` relates the attention call's algorithmic bytes
 out) to its measured duration against the 8 TB/s HBM peak. ``cpu_baseline`` times the
 float64 CPU oracle on whole verify calls of the same workload (about 10 s of CPU work).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-check]
+``--workload`` times another configuration of the workload set the same way (a profiling
+aid; the default line is the 128K one). A call whose flops per algorithmic byte exceed the
+ridge point of the two peaks (2.5 PFLOP/s dense bf16 over 8 TB/s, 312.5 flop/B), as for the
+256-node tree, reports an MFMA roofline: 4 * nodes * q heads * keys * head dim flops per
+call against the bf16 peak.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+       [--no-check]
 """
 
 from __future__ import annotations
@@ -27,6 +34,7 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16, MI355X
 LAYERS = 64
 WORKLOAD = "long_128k"
 CPU_SAMPLE_SECONDS = 10.0
@@ -68,6 +76,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-check", action="store_true", help="skip the parity re-check")
     ap.add_argument("--layers", type=int, default=LAYERS)
+    ap.add_argument("--workload", default=WORKLOAD,
+                    help="configuration to time (profiling aid; the reported metric is long_128k's)")
     ap.add_argument("--splits", type=int, default=0, help="force the KV split count (0 = library choice)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one device copy of this many MiB (counter calibration)")
@@ -81,8 +91,8 @@ def log(msg):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: the verify step is measured per device "
-              "(multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the verify step is measured per device; a "
+              "multi-GPU layout (KV heads split across GPUs, no exchange) is not built", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -96,7 +106,7 @@ def main():
     tv.lib()
 
     log("generating the seeded workload (CPU)")
-    w = make(WORKLOAD, 0)
+    w = make(args.workload, 0)
     N, L, Hq, Hkv, D, V = w.N, w.L, w.Hq, w.Hkv, w.D, w.V
     T = L + N
 
@@ -246,6 +256,21 @@ def main():
     qo_bytes = 2 * N * Hq * D * 2
     algo_bytes = kv_bytes + qo_bytes
     achieved = algo_bytes / (t_attn_mean_us * 1e-6) / 1e9
+    flops = 4 * N * Hq * T * D
+    # The roofline that bounds the call: HBM for long contexts, MFMA for wide trees
+    # (arithmetic intensity above the 312 flop/B ridge of 2.5 PFLOP/s over 8 TB/s).
+    mfma_bound = flops / algo_bytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        roofline = {"bound": "mfma", "achieved": round(flops / (t_attn_mean_us * 1e-6) / 1e12, 1),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(flops / (t_attn_mean_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": None, "kernel": "tv_tree_attn (split + merge)", "algorithmic_flops": flops}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic() if args.workload == WORKLOAD else None,
+                    "kernel": "tv_tree_attn (split + merge)", "algorithmic_bytes": algo_bytes,
+                    "traffic_unit": "bytes per call"}
     kv_gbps = kv_bytes / (t_attn_us * 1e-6) / 1e9
     log(f"attn {t_attn_us:.1f} us/call ({kv_gbps:.0f} GB/s KV, {kv_gbps / HBM_PEAK_GBS:.1%} of peak), "
         f"argmax+accept {t_tokens_us:.1f} us, step {ms_per_step:.2f} ms (graph replay {graph_ms_per_step:.2f} ms)")
@@ -332,9 +357,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "long_128k: KV 131072 + 64-node tree (depth<=16), 32 q / 8 KV heads, D=128, "
-                               "bf16; logits [64,152064] bf16; 64 layer-equivalent attention calls on distinct "
-                               "KV buffers + argmax + accept per step",
+        "config": {"workload": ("long_128k: KV 131072 + 64-node tree (depth<=16), 32 q / 8 KV heads, D=128, "
+                                "bf16; logits [64,152064] bf16; 64 layer-equivalent attention calls on distinct "
+                                "KV buffers + argmax + accept per step") if args.workload == WORKLOAD else
+                               (f"{args.workload}: KV {L} + {N} nodes, {Hq} q / {Hkv} KV heads, D={D}, bf16; logits "
+                                f"[{N},{V}]; {layers} layer-equivalent attention calls on distinct KV buffers + "
+                                f"argmax + accept per step"),
                    "kv_len": L, "nodes": N, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "vocab": V,
                    "layers_per_step": layers, "parallelism": "none (1 GPU)"},
         "breakdown_us": {"attn_per_call": round(t_attn_us, 2), "attn_mean": round(t_attn_mean_us, 2),
@@ -347,10 +375,7 @@ def main():
         "kv_gbps": round(kv_gbps, 1),
         "kv_hbm_frac": round(kv_gbps / HBM_PEAK_GBS, 4),
         "hbm_copy_gbps": round(copy_gbps, 1),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "tv_tree_attn (split + merge)", "algorithmic_bytes": algo_bytes,
-                     "traffic_unit": "bytes per call"},
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,
     }
