@@ -293,9 +293,10 @@ __global__ __launch_bounds__(kBlock) void sample_partial(const char* __restrict_
 // the row argmax (loads batched 32 slices at a time, one round trip for vocabularies up to
 // 262144 bf16 entries; indices clamped so that no load is conditional, and a repeated
 // (value, index) pair cannot change the result), keeps the tokens
-// in LDS and runs the acceptance walk on them (the walk of tv_accept). The tree
-// preprocessing and the draft loads are issued first so that their latency overlaps the
-// reduction. With a single slice per row the slice kernel already wrote tok.
+// in LDS and runs the acceptance walk on them (the walk of tv_accept). The draft and
+// parent entries and the first batch of slice results are loaded together, ahead of the
+// tree preprocessing, so that their round trips overlap. With a single slice per row the
+// slice kernel already wrote tok.
 constexpr int kFuseThreads = kMaxNodes;
 
 __global__ __launch_bounds__(kFuseThreads) void argmax_accept_kernel(
@@ -311,22 +312,34 @@ __global__ __launch_bounds__(kFuseThreads) void argmax_accept_kernel(
   __shared__ int32_t tok_s[kMaxNodes];
   const int i = threadIdx.x;
   const int draft_i = i < N ? draft[i] : 0;
-  tree_prep_lds(parent, N, anc, par, jmp, dev_error);
+  const int parent_i = i < N ? parent[i] : -1;
+  const bool reduce = i < N && chunks > 1;
+  const float* pv = part_v + (int64_t)(reduce ? i : 0) * chunks;
+  const int* pi = part_i + (int64_t)(reduce ? i : 0) * chunks;
+  float v[32];
+  int ix[32];
+  if (reduce) {
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int j = min(u, chunks - 1);
+      v[u] = pv[j];
+      ix[u] = pi[j];
+    }
+  }
+  tree_prep_lds_from(parent_i, N, anc, par, jmp, dev_error);
 
   if (i < N) {
     int32_t t;
     if (chunks > 1) {
-      const float* pv = part_v + (int64_t)i * chunks;
-      const int* pi = part_i + (int64_t)i * chunks;
       Best b{-INFINITY, INT_MAX};
       for (int j0 = 0; j0 < chunks; j0 += 32) {
-        float v[32];
-        int ix[32];
+        if (j0 > 0) {
 #pragma unroll
-        for (int u = 0; u < 32; ++u) {
-          const int j = min(j0 + u, chunks - 1);
-          v[u] = pv[j];
-          ix[u] = pi[j];
+          for (int u = 0; u < 32; ++u) {
+            const int j = min(j0 + u, chunks - 1);
+            v[u] = pv[j];
+            ix[u] = pi[j];
+          }
         }
 #pragma unroll
         for (int u = 0; u < 32; ++u) b = better(b, Best{v[u], ix[u]});

@@ -30,14 +30,16 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 //   par[i]        parent[i] clamped to -1 when outside [-1, i-1].
 // A clamped entry stores TV_ERR_BAD_TREE into *dev_error when dev_error is non-null.
 // Ancestor sets are built by pointer jumping: anc[i] always holds the path from i up to
-// (not including) jmp[i]; each round doubles the jump, so 8 rounds cover depth 256.
+// (not including) jmp[i]; each round doubles the jump. A path holds at most N nodes
+// (parent[i] < i), so ceil(log2 N) rounds complete every set.
 // Requires blockDim.x >= N; every thread of the block must call it (it synchronises).
-__device__ __forceinline__ void tree_prep_lds(const int32_t* __restrict__ parent, int N,
-                                              uint64_t* anc, int* par, int* jmp,
-                                              int32_t* dev_error) {
+// tree_prep_lds_from takes thread i's entry parent[i] already loaded (ignored for i >= N),
+// so that a caller can have other loads in flight behind it; tree_prep_lds loads it.
+__device__ __forceinline__ void tree_prep_lds_from(int parent_i, int N, uint64_t* anc, int* par, int* jmp,
+                                                   int32_t* dev_error) {
   const int i = threadIdx.x;
   if (i < N) {
-    int p = parent[i];
+    int p = parent_i;
     if (p < -1 || p >= i) {
       p = -1;
       if (dev_error) *dev_error = TV_ERR_BAD_TREE;
@@ -48,7 +50,8 @@ __device__ __forceinline__ void tree_prep_lds(const int32_t* __restrict__ parent
     for (int w = 0; w < kAncWords; ++w) anc[i * kAncWords + w] = (w == (i >> 6)) ? (1ull << (i & 63)) : 0ull;
   }
   __syncthreads();
-  for (int round = 0; round < 8; ++round) {
+  const int rounds = N > 1 ? 32 - __clz(N - 1) : 0;  // ceil(log2 N), uniform
+  for (int round = 0; round < rounds; ++round) {
     uint64_t a[kAncWords];
     int next = -1;
     if (i < N) {
@@ -69,6 +72,12 @@ __device__ __forceinline__ void tree_prep_lds(const int32_t* __restrict__ parent
     }
     __syncthreads();
   }
+}
+
+__device__ __forceinline__ void tree_prep_lds(const int32_t* __restrict__ parent, int N, uint64_t* anc, int* par,
+                                              int* jmp, int32_t* dev_error) {
+  const int i = threadIdx.x;
+  tree_prep_lds_from(i < N ? parent[i] : -1, N, anc, par, jmp, dev_error);
 }
 
 __device__ __forceinline__ int anc_popcount(const uint64_t* anc, int i) {
