@@ -45,10 +45,10 @@ CPU_SAMPLE_SECONDS = 10.0
 # profiles/tv_tree_attn_long_128k_hbm_counters.md. Valid only for the kernel sources they
 # were taken on (compared through a digest of their code without comments): reported as
 # null once that code changes.
-TRAFFIC_BYTES_PER_CALL = 608159372
+TRAFFIC_BYTES_PER_CALL = 607770506
 TRAFFIC_SOURCES = ("draft_tree_verification_tv_amd/csrc/tv_attn.hip",
                    "draft_tree_verification_tv_amd/csrc/tv_internal.h")
-TRAFFIC_SOURCES_SHA256 = "4b38ebbb402a6953e14c2f276d4aabd7c0ae04d0b47b19296959b7342659344b"
+TRAFFIC_SOURCES_SHA256 = "0d96ab916c63a4fdf50c25dfc618e02c470c972c7e538f57c0d94bf5ed8e8eb7"
 
 
 def code_digest(root, files):

@@ -351,8 +351,6 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
   f32x16 sc[2];             // scores of two consecutive 32-key blocks
   bf16x8 pb[2];             // P^T fragments of the current block (two 16-key steps)
 
-  // Scheduling masks for __builtin_amdgcn_sched_group_barrier.
-
   // bf16 tiles of tile t in LDS.
   auto kstage = [&](int t) __attribute__((always_inline)) -> const char* {
     if constexpr (kF8)
