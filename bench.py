@@ -45,10 +45,10 @@ CPU_SAMPLE_SECONDS = 10.0
 # profiles/tv_tree_attn_long_128k_hbm_counters.md. Valid only for the kernel sources they
 # were taken on (compared through a digest of their code without comments): reported as
 # null once that code changes.
-TRAFFIC_BYTES_PER_CALL = 607770506
+TRAFFIC_BYTES_PER_CALL = 607593162
 TRAFFIC_SOURCES = ("draft_tree_verification_tv_amd/csrc/tv_attn.hip",
                    "draft_tree_verification_tv_amd/csrc/tv_internal.h")
-TRAFFIC_SOURCES_SHA256 = "0d96ab916c63a4fdf50c25dfc618e02c470c972c7e538f57c0d94bf5ed8e8eb7"
+TRAFFIC_SOURCES_SHA256 = "55f09d5cdabbcc6b3b34821baf9f6c30bc0d6be06c34a2174e2530b0d604daa9"
 
 
 def code_digest(root, files):

@@ -806,6 +806,48 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams mp) {
   if (mp.lse && lane == 0) mp.lse[row] = mx == -INFINITY ? -INFINITY : (mx + __log2f(wsum)) * kLn2;
 }
 
+// The same merge for up to 64 splits in one memory round trip: the split log-sum-exps and
+// all NB * 16 partial-output loads (addresses clamped to the last split) are issued before
+// any of them is used.
+template <int NB>
+__global__ __launch_bounds__(256) void attn_merge_small_kernel(MergeParams mp) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= mp.N * mp.Hq) return;
+  const int n = row / mp.Hq;
+  const int qh = row % mp.Hq;
+  const int h = qh / mp.G;
+  const int r = n * mp.G + qh % mp.G;
+  const int rt = r / mp.rows;
+  const int64_t base0 = (int64_t)(h * mp.RT + rt) * mp.S * TILE_ROWS + (r % mp.rows);
+  const float* lse_p = mp.part_lse + base0;
+  const float* o_p = mp.part_o + base0 * D + 2 * lane;
+  const int S = mp.S;  // 1 .. NB * 16
+
+  const float l = lane < S ? lse_p[(int64_t)lane * TILE_ROWS] : -INFINITY;
+  f32x2 x[NB * 16];
+#pragma unroll
+  for (int u = 0; u < NB * 16; ++u)
+    x[u] = *reinterpret_cast<const f32x2*>(o_p + (int64_t)min(u, S - 1) * TILE_ROWS * D);
+
+  float mx = l;
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  const float w = (lane < S && mx != -INFINITY) ? exp2f(l - mx) : 0.f;
+  float wsum = w;
+  for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
+  f32x2 acc = {0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < NB * 16; ++u) {
+    const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
+    acc += wu * x[u];  // lanes >= S carry weight 0
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const bf16x2 ob = __builtin_convertvector((f32x2{acc[0] * inv, acc[1] * inv}), bf16x2);
+  *reinterpret_cast<bf16x2*>(mp.out + (int64_t)row * D + 2 * lane) = ob;
+  if (mp.lse && lane == 0) mp.lse[row] = mx == -INFINITY ? -INFINITY : (mx + __log2f(wsum)) * kLn2;
+}
+
 template <int RWV, bool kF8>
 hipError_t launch_split(const SplitParams& sp, int nwg, hipStream_t stream) {
   constexpr int KSW = 8 / RWV;
@@ -926,7 +968,14 @@ hipError_t launch_attn(const AttnPlan& plan, bool f8, const void* q, const void*
   mp.S = plan.S;
   mp.rows = plan.RWV * 32;
   const int rows_out = N * Hq;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3((rows_out + 3) / 4), dim3(256), 0, stream, mp);
+  const dim3 mgrid((rows_out + 3) / 4);
+  switch ((plan.S + 15) / 16) {
+    case 1: hipLaunchKernelGGL(attn_merge_small_kernel<1>, mgrid, dim3(256), 0, stream, mp); break;
+    case 2: hipLaunchKernelGGL(attn_merge_small_kernel<2>, mgrid, dim3(256), 0, stream, mp); break;
+    case 3: hipLaunchKernelGGL(attn_merge_small_kernel<3>, mgrid, dim3(256), 0, stream, mp); break;
+    case 4: hipLaunchKernelGGL(attn_merge_small_kernel<4>, mgrid, dim3(256), 0, stream, mp); break;
+    default: hipLaunchKernelGGL(attn_merge_kernel, mgrid, dim3(256), 0, stream, mp); break;
+  }
   return hipGetLastError();
 }
 

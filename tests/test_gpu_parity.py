@@ -242,9 +242,12 @@ def test_attention_edge_shapes(label, ov):
     check_attention(out, ref, lse, lref, label)
 
 
-@pytest.mark.parametrize("splits", [1, 2, 3, 7, 40, 1024])
+# T = 7022 keys, 110 tiles: the requests below give 1, 2, 3, 7, 19, 37, 55 and 110 splits,
+# i.e. every 16-split batch count of the single-round-trip merge (up to 64 splits) and the
+# chunked merge beyond.
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 20, 40, 55, 1024])
 def test_attention_forced_splits(splits):
-    w = make("budget22", 11, L=2500, N=22)
+    w = make("budget22", 11, L=7000, N=22)
     note(f"attention forced splits {splits}")
     out, lse = attn_gpu(w, num_splits=splits)
     ref, lref = attn_ref(w)
