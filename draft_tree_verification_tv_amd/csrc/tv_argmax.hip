@@ -186,6 +186,11 @@ __global__ __launch_bounds__(256) void argmax_final(int N, int chunks, const flo
 // come from Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
 // as 1, 2, 3", SC 2011): key (seed lo, seed hi), counter (v / 4, node, offset lo, offset
 // hi); word v % 4 gives u = ((word >> 9) + 0.5) / 2^23, exact in float32.
+//
+// The kernel ranks log2-domain scores, logit * log2(e) / T - log2(-log2 u). That is
+// (score - ln ln 2) / ln 2 for the natural-log score above: an increasing map, so the
+// argmax is the same, and it costs one fma and two hardware log2 instructions per entry.
+// u >= 2^-24 and -log2 u >= 2^-24 / ln 2, so neither logarithm sees a denormal.
 
 __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
                                                uint32_t k1) {
@@ -205,12 +210,12 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 
 struct SampleKey {
   uint32_t k0, k1, o0, o1;  // seed and offset halves
-  float inv_t;              // 1 / temperature
+  float c;                  // log2(e) / temperature
 };
 
-__device__ __forceinline__ float gumbel_score(float x, uint32_t word, float inv_t) {
+__device__ __forceinline__ float gumbel_score(float x, uint32_t word, float c) {
   const float u = ((float)(word >> 9) + 0.5f) * 0x1p-23f;
-  return __builtin_fmaf(x, inv_t, -__logf(-__logf(u)));
+  return __builtin_fmaf(x, c, -__builtin_amdgcn_logf(-__builtin_amdgcn_logf(u)));
 }
 
 // Grid (slices, rows), 256 threads; the slice layout and outputs are those of
@@ -259,7 +264,7 @@ __global__ __launch_bounds__(kBlock) void sample_partial(const char* __restrict_
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (e + j < end) {
-        const float sc = gumbel_score(x[j], j < 4 ? r0[j] : r1[j - 4], key.inv_t);
+        const float sc = gumbel_score(x[j], j < 4 ? r0[j] : r1[j - 4], key.c);
         if (sc > b.v || b.i == INT_MAX) {
           b.v = sc;
           b.i = e + j;
@@ -456,7 +461,7 @@ hipError_t launch_sample_accept(const void* logits, int dtype, int N, int V, int
   float* part_v = reinterpret_cast<float*>(ws);
   int* part_i = reinterpret_cast<int*>(ws + (parts * sizeof(float) + 255) / 256 * 256);
   SampleKey key{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)offset, (uint32_t)(offset >> 32),
-                1.0f / temperature};
+                (float)(1.4426950408889634 / (double)temperature)};
   const dim3 grid(p.chunks, N);
   const char* lg = static_cast<const char*>(logits);
   if (dtype == TV_F32) {
