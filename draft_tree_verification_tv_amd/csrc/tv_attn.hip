@@ -686,29 +686,34 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
   }
 
   // ---- key-waves: merge the KSW partial states of each row in LDS (the ring is free:
-  // every copy has landed and every wave has finished its reads at the barrier). Each
-  // key-wave k > 0 leaves O (64 values per lane, lane-interleaved), its reference maximum
-  // and its row-sum part; key-wave 0 rescales all to the common maximum and adds them.
+  // every copy has landed and every wave has finished its reads at the barrier), as a
+  // tree: in each round the upper half of the remaining key-waves leaves O (64 values per
+  // lane, lane-major with a 68-float pitch so that the 16-byte accesses of 16 lanes cover
+  // all 64 banks once), its reference maximum and its row-sum part, and the lower half
+  // rescales both states to the common maximum and adds them. log2(KSW) rounds.
   if constexpr (KSW > 1) {
-    barrier_keep<0>();
-    constexpr int SLOT = 64 * 64 + 128;  // floats per (row-wave, key-wave)
+    constexpr int PITCH = 68;
+    constexpr int SLOT = 64 * PITCH + 128;  // floats per (row-wave, writer)
     float* ms = reinterpret_cast<float*>(smem);
-    if (kw > 0) {
-      float* b = ms + ((kw - 1) * RWV + rw) * SLOT;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+    for (int half = KSW / 2; half >= 1; half /= 2) {
+      barrier_keep<0>();
+      if (kw >= half && kw < 2 * half) {
+        float* b = ms + ((kw - half) * RWV + rw) * SLOT;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) b[(db * 16 + i) * 64 + lane] = o[db][i];
-      b[4096 + lane] = m_ref;
-      b[4096 + 64 + lane] = lsum;
-    }
-    barrier_keep<0>();
-    if (kw == 0) {
-#pragma unroll 1
-      for (int k = 1; k < KSW; ++k) {
-        const float* b = ms + ((k - 1) * RWV + rw) * SLOT;
-        const float mk = b[4096 + lane];
-        const float lk = b[4096 + 64 + lane];
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; i += 4)
+            *reinterpret_cast<f32x4*>(b + lane * PITCH + db * 16 + i) =
+                f32x4{o[db][i], o[db][i + 1], o[db][i + 2], o[db][i + 3]};
+        b[64 * PITCH + lane] = m_ref;
+        b[64 * PITCH + 64 + lane] = lsum;
+      }
+      barrier_keep<0>();
+      if (kw < half) {
+        const float* b = ms + (kw * RWV + rw) * SLOT;
+        const float mk = b[64 * PITCH + lane];
+        const float lk = b[64 * PITCH + 64 + lane];
         const float mn = fmaxf(m_ref, mk);
         const float a0 = m_ref == -INFINITY ? 0.f : exp2f(m_ref - mn);
         const float ak = mk == -INFINITY ? 0.f : exp2f(mk - mn);
@@ -716,7 +721,11 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[db][i] = o[db][i] * a0 + b[(db * 16 + i) * 64 + lane] * ak;
+          for (int i = 0; i < 16; i += 4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(b + lane * PITCH + db * 16 + i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[db][i + j] = o[db][i + j] * a0 + v[j] * ak;
+          }
         m_ref = mn;
       }
     }
