@@ -11,11 +11,13 @@
 //     is used by every row that needs it. A workgroup always runs 8 waves: RWV row-waves
 //     of 32 rows times KSW key-waves (8x1 for M > 128; 4x2, 2x4, 1x8 for fewer rows).
 //     Key-wave k takes every KSW-th 32-key block of the split with its own online
-//     softmax; the key-waves' partial results are merged in LDS at the end, so small
-//     trees and single-token decode still keep two waves busy on every SIMD.
+//     softmax; the key-waves' partial results are merged in LDS at the end (a tree of
+//     log2 KSW rounds), so small trees and single-token decode still keep two waves busy
+//     on every SIMD.
 //   * Splits. The key sequence [0, L+N) is cut into S ranges; each workgroup streams one
 //     range for one (KV head, row tile) and writes a normalised fp32 partial output and
-//     its log2-sum-exp. attn_merge_kernel combines the partials.
+//     its log2-sum-exp. attn_merge_small_kernel (up to 64 splits, one memory round trip)
+//     or attn_merge_kernel combines the partials.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: the
 //     accumulator layout gives every lane one query row (16 keys per 32-key block), so the
 //     online-softmax statistics are lane-local (plus one exchange with lane ^ 32), and
