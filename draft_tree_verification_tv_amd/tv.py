@@ -96,13 +96,21 @@ def _check(status: int, where: str):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # The prototypes declare c_void_p, so ctypes takes the address as a plain int.
+    return None if t is None else t.data_ptr()
+
+
+# torch's raw current-stream query skips building a Stream object (a few µs per call,
+# which matters for calls whose kernels take about 10 µs); the public route otherwise.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(stream):
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _need_cuda(name, t, dtype=None):
@@ -165,8 +173,8 @@ def tree_attn(q, k, v, parent, L=None, scale=None, num_splits=0, out=None, lse=N
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((N, Hq, D), dtype=torch.bfloat16, device=q.device)
-    ws_bytes = tree_attn_workspace_size(N, L, Hq, Hkv, D, num_splits)
     if workspace is None:
+        ws_bytes = tree_attn_workspace_size(N, L, Hq, Hkv, D, num_splits)
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
     _check(lib().tv_tree_attn(_ptr(q), _ptr(k), _ptr(v), k.stride(0), k.stride(1), _ptr(parent), N, L, Hq,
                               Hkv, D, float(scale), int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace),
@@ -205,8 +213,8 @@ def tree_attn_fp8(q, k_codes, v_codes, k_exps, v_exps, parent, L=None, scale=Non
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((N, Hq, D), dtype=torch.bfloat16, device=q.device)
-    ws_bytes = tree_attn_workspace_size(N, L, Hq, Hkv, D, num_splits)
     if workspace is None:
+        ws_bytes = tree_attn_workspace_size(N, L, Hq, Hkv, D, num_splits)
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
     _check(lib().tv_tree_attn_fp8(_ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_exps), _ptr(v_exps),
                                   k_codes.stride(0), k_codes.stride(1), _ptr(parent), N, L, Hq, Hkv, D,
