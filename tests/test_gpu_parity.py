@@ -275,6 +275,27 @@ def test_attention_strided_cache():
     check_attention(out, ref, label="strided")
 
 
+def test_binding_uses_the_current_stream():
+    """A call without an explicit stream runs on torch's current stream. On a side stream
+    the query is overwritten behind a spin of several milliseconds, then attention reads
+    it: only a launch on that same stream sees the new query."""
+    w = make("budget22", 5)
+    q_new_bits = np.ascontiguousarray(np.flip(w.q, axis=1))
+    k, v, parent = dev_bf16(w.k), dev_bf16(w.v), dev_i32(w.parent)
+    q = dev_bf16(w.q)
+    q_new = dev_bf16(q_new_bits)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)
+        q.copy_(q_new)
+        out = tv.tree_attn(q, k, v, parent, L=w.L, scale=w.scale)
+    side.synchronize()
+    ref, _ = oracle.tree_attention(oracle.bf16_bits_to_f64(q_new_bits), oracle.bf16_bits_to_f64(w.k),
+                                   oracle.bf16_bits_to_f64(w.v), w.parent, w.scale)
+    check_attention(out, ref, None, None, "side stream")
+
+
 def test_attention_bad_tree_flag():
     w = make("budget22", 2, L=200)
     bad = w.parent.copy()
