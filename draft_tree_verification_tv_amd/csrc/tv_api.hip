@@ -176,7 +176,8 @@ int tv_sample_accept(const void* logits, int dtype, int N, int V, int64_t row_st
     return TV_ERR_INVALID_ARG;
   if (N < 1 || N > TV_MAX_NODES || V < 1 || V >= INT32_MAX - 8 || row_stride < V) return TV_ERR_INVALID_ARG;
   if (dtype != TV_BF16 && dtype != TV_F32) return TV_ERR_INVALID_ARG;
-  if (!(temperature > 0.f) || !std::isfinite(temperature) || !std::isfinite(1.0f / temperature))
+  if (!(temperature > 0.f) || !std::isfinite(temperature) ||
+      !std::isfinite((float)(1.4426950408889634 / (double)temperature)))
     return TV_ERR_INVALID_ARG;
   const size_t need = tv::argmax_workspace_bytes(N, V);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return TV_ERR_WORKSPACE;

@@ -197,7 +197,10 @@ int tv_argmax_accept(const void* logits, int dtype, int N, int V, int64_t row_st
  * (seed low, seed high) and counter (v / 4, i, offset low, offset high): word v % 4 of the
  * output gives u = ((word >> 9) + 0.5) / 2^23. The same (seed, offset) repeats the draw;
  * advance offset between steps. Acceptance then follows tv_accept on these tokens.
- *   temperature  > 0, finite, with 1/T finite.
+ * The kernel ranks the equivalent scores logits[i][v] * log2(e) / T - log2(-log2 u) in
+ * float32 (one fma and two hardware log2 per entry), so among scores equal after float32
+ * rounding the lowest index wins.
+ *   temperature  > 0, finite, with log2(e) / T finite in float32 (else TV_ERR_INVALID_ARG).
  *   Other arguments and limits as for tv_argmax_accept (same workspace size).
  */
 int tv_sample_accept(const void* logits, int dtype, int N, int V, int64_t row_stride,

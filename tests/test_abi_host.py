@@ -188,7 +188,8 @@ def test_kv_commit_rejects(args, status):
     assert tv.lib().tv_kv_commit(*args, None, None, None) == status
 
 
-@pytest.mark.parametrize("temp", [0.0, -1.0, float("inf"), float("nan"), 1e-45])
+# 3.5e-39: 1/T fits in float32 but log2(e)/T, the factor the kernel applies, does not.
+@pytest.mark.parametrize("temp", [0.0, -1.0, float("inf"), float("nan"), 1e-45, 3.5e-39])
 def test_sample_accept_rejects_bad_temperature(temp):
     L = tv.lib()
     assert L.tv_sample_accept(FAKE, 0, 4, 100, 100, temp, 1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
