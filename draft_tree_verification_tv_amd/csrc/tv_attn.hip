@@ -107,7 +107,7 @@ struct SplitParams {
   int N, L, T, Hq, G, M;
   int RT, S, KS;
   float c;  // scale * log2(e)
-  float* part_o;
+  __bf16* part_o;  // normalised partial outputs, bf16
   float* part_lse;
   int32_t* dev_error;
   int remap;
@@ -742,14 +742,14 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
   const float lse2 = lsum > 0.f ? m_ref + __log2f(lsum) : -INFINITY;
   if (rvalid && kw == 0) {
     const int64_t base = ((int64_t)(h * p.RT + rt) * p.S + s) * TILE_ROWS + rw * 32 + ql;
-    float* po = p.part_o + base * D;
+    __bf16* po = p.part_o + base * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const f32x4 val = {o[db][4 * i] * inv, o[db][4 * i + 1] * inv, o[db][4 * i + 2] * inv,
                            o[db][4 * i + 3] * inv};
-        *reinterpret_cast<f32x4*>(po + db * 32 + 8 * i + 4 * grp) = val;
+        *reinterpret_cast<bf16x4*>(po + db * 32 + 8 * i + 4 * grp) = __builtin_convertvector(val, bf16x4);
       }
     }
     if (grp == 0) p.part_lse[base] = lse2;
@@ -757,7 +757,7 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
 }
 
 struct MergeParams {
-  const float* part_o;
+  const __bf16* part_o;
   const float* part_lse;
   uint16_t* out;
   float* lse;
@@ -782,7 +782,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams mp) {
   const int rt = r / mp.rows;
   const int64_t base0 = (int64_t)(h * mp.RT + rt) * mp.S * TILE_ROWS + (r % mp.rows);
   const float* lse_p = mp.part_lse + base0;
-  const float* o_p = mp.part_o + base0 * D + 2 * lane;
+  const __bf16* o_p = mp.part_o + base0 * D + 2 * lane;
 
   float mx = -INFINITY;
   for (int s = lane; s < mp.S; s += 64) mx = fmaxf(mx, lse_p[(int64_t)s * TILE_ROWS]);
@@ -800,7 +800,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams mp) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
           const int sj = s0 + min(j + u, cnt - 1);
-          x[u] = *reinterpret_cast<const f32x2*>(o_p + (int64_t)sj * TILE_ROWS * D);
+          x[u] = __builtin_convertvector(*reinterpret_cast<const bf16x2*>(o_p + (int64_t)sj * TILE_ROWS * D), f32x2);
         }
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
@@ -833,14 +833,15 @@ __global__ __launch_bounds__(256) void attn_merge_small_kernel(MergeParams mp) {
   const int rt = r / mp.rows;
   const int64_t base0 = (int64_t)(h * mp.RT + rt) * mp.S * TILE_ROWS + (r % mp.rows);
   const float* lse_p = mp.part_lse + base0;
-  const float* o_p = mp.part_o + base0 * D + 2 * lane;
+  const __bf16* o_p = mp.part_o + base0 * D + 2 * lane;
   const int S = mp.S;  // 1 .. NB * 16
 
   const float l = lane < S ? lse_p[(int64_t)lane * TILE_ROWS] : -INFINITY;
   f32x2 x[NB * 16];
 #pragma unroll
   for (int u = 0; u < NB * 16; ++u)
-    x[u] = *reinterpret_cast<const f32x2*>(o_p + (int64_t)min(u, S - 1) * TILE_ROWS * D);
+    x[u] = __builtin_convertvector(*reinterpret_cast<const bf16x2*>(o_p + (int64_t)min(u, S - 1) * TILE_ROWS * D),
+                                   f32x2);
 
   float mx = l;
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
@@ -906,9 +907,9 @@ AttnPlan attn_plan(int N, int L, int Hq, int Hkv, int num_splits, int num_cus) {
 
 size_t attn_workspace_bytes(const AttnPlan& p, int Hkv) {
   const size_t rows = (size_t)Hkv * p.RT * p.S * TILE_ROWS;
-  size_t bytes = rows * D * sizeof(float);
+  size_t bytes = rows * D * sizeof(__bf16);  // partial outputs
   bytes = (bytes + 255) / 256 * 256;
-  bytes += rows * sizeof(float);
+  bytes += rows * sizeof(float);              // partial log2-sum-exps
   return (bytes + 255) / 256 * 256;
 }
 
@@ -920,8 +921,8 @@ hipError_t launch_attn(const AttnPlan& plan, bool f8, const void* q, const void*
                        int32_t* dev_error, hipStream_t stream) {
   const size_t rows = (size_t)Hkv * plan.RT * plan.S * TILE_ROWS;
   char* ws = static_cast<char*>(workspace);
-  float* part_o = reinterpret_cast<float*>(ws);
-  float* part_lse = reinterpret_cast<float*>(ws + (rows * D * sizeof(float) + 255) / 256 * 256);
+  __bf16* part_o = reinterpret_cast<__bf16*>(ws);
+  float* part_lse = reinterpret_cast<float*>(ws + (rows * D * sizeof(__bf16) + 255) / 256 * 256);
 
   SplitParams sp;
   sp.q = static_cast<const uint16_t*>(q);

@@ -106,8 +106,9 @@ int tv_tree_prep(const int32_t* parent, int N, uint64_t* anc, int32_t* depth,
  *               the same num_splits; 16-byte aligned. Contents need no initialisation.
  * Limits: 1 <= N <= TV_MAX_NODES, L >= 0, D == TV_HEAD_DIM, Hkv >= 1, Hq % Hkv == 0,
  * num_splits in [0, 1024], scale > 0 and finite; (L + N) * kv_stride_t * 2 bytes must stay
- * below 4 GiB (TV_ERR_UNSUPPORTED otherwise). Accumulation is fp32; inputs are never
- * modified.
+ * below 4 GiB (TV_ERR_UNSUPPORTED otherwise). Accumulation is fp32; each KV split's
+ * normalised partial output passes through the workspace as bf16 (its log-sum-exp as
+ * fp32). Inputs are never modified.
  */
 size_t tv_tree_attn_workspace_size(int N, int L, int Hq, int Hkv, int D, int num_splits);
 
