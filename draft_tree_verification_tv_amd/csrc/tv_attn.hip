@@ -13,7 +13,9 @@
 //     Key-wave k takes every KSW-th 32-key block of the split with its own online
 //     softmax; the key-waves' partial results are merged in LDS at the end (a tree of
 //     log2 KSW rounds), so small trees and single-token decode still keep two waves busy
-//     on every SIMD.
+//     on every SIMD. With a single row-wave (bf16 cache) each 32-key block has one
+//     reader, so every wave streams its own blocks (K into registers, V through a private
+//     LDS stage) with no shared ring and no barrier.
 //   * Splits. The key sequence [0, L+N) is cut into S ranges; each workgroup streams one
 //     range for one (KV head, row tile) and writes a normalised fp32 partial output and
 //     its log2-sum-exp. attn_merge_small_kernel (up to 64 splits, one memory round trip)
@@ -626,6 +628,58 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
     }
     }
     if (__any(bad_exp) && lane == 0 && p.dev_error) *p.dev_error = TV_ERR_INVALID_ARG;
+  } else if constexpr (RWV == 1) {
+    // ---- one row-wave (M <= 32): every 32-key block has a single reader, so each wave
+    // streams its own blocks b = wave, wave + 8, ... with no shared ring and no barrier.
+    // K goes straight into registers as MFMA A fragments (two buffers, one block ahead);
+    // V is copied into two private 8 KB LDS stages for the transposed reads.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    constexpr int VB = 32 * ROWB;  // one V block
+    const int nblk = (kend - kbeg + 31) / 32;
+    const uint32_t vpriv = lds_base + (uint32_t)(wave * 2 * VB);
+    const char* vprivp = smem + wave * 2 * VB;
+    bf16x8 kf0[8], kf1[8];
+    auto load_block = [&](int b, bf16x8(&kf)[8], int stage) __attribute__((always_inline)) {
+      const int key = min(kbeg + b * 32 + ql, p.T - 1);
+      const char* row = kb8 + (uint32_t)key * rowstride_b + grp * 16;
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8) kf[s8] = *reinterpret_cast<const bf16x8*>(row + s8 * 32);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 4 * j + (lane >> 4);
+        const int pc = lane & 15;
+        const uint32_t grow = (uint32_t)min(kbeg + b * 32 + r, p.T - 1) * rowstride_b;
+        dma16(vpriv + (uint32_t)(stage * VB + j * 1024), grow + (uint32_t)((pc ^ swz_v(r)) << 4), vb8);
+      }
+    };
+    auto compute_block = [&](int b, const bf16x8(&kf)[8], int stage) __attribute__((always_inline)) {
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8) acc = mfma32(kf[s8], qf[s8], acc);
+      sc[0] = acc;
+      if (kbeg + b * 32 + 32 > p.L) mask(kbeg + b * 32, 0);
+      softmax(0);
+      pv(vprivp + stage * VB - VBASE, 0);
+    };
+    int b = wave;
+    if (b < nblk) load_block(b, kf0, 0);
+    for (; b < nblk; b += 16) {
+      if (b + 8 < nblk) {
+        load_block(b + 8, kf1, 1);
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      compute_block(b, kf0, 0);
+      if (b + 8 >= nblk) break;
+      if (b + 16 < nblk) {
+        load_block(b + 16, kf0, 0);
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      compute_block(b + 8, kf1, 1);
+    }
   } else if constexpr (KSW > 1) {
     // ---- key-waves: tiles 0, 1, 2 start streaming; tiles 0 and 1 must land.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
