@@ -254,6 +254,19 @@ def test_attention_forced_splits(splits):
     check_attention(out, ref, lse, lref, f"splits={splits}")
 
 
+# One row-wave (N * G <= 32): every wave streams its own 32-key blocks. T = 5001 keys, 79
+# tiles: the requests give 1, 4, 40 and 79 splits of 158, 40, 4 and 2 blocks (the last
+# split's final block is cut by the end of the keys), so with 4 or 2 blocks most waves
+# have none.
+@pytest.mark.parametrize("splits", [1, 4, 40, 1024])
+def test_attention_single_row_wave_splits(splits):
+    w = make("decode_1node", 3, L=5000)
+    note(f"attention decode forced splits {splits}")
+    out, lse = attn_gpu(w, num_splits=splits)
+    ref, lref = attn_ref(w)
+    check_attention(out, ref, lse, lref, f"decode splits={splits}")
+
+
 def test_attention_peaky_keys():
     w = make("max_256k", 1, L=20000)
     note("attention peaky 20k")
