@@ -632,7 +632,11 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
     // ---- one row-wave (M <= 32): every 32-key block has a single reader, so each wave
     // streams its own blocks b = wave, wave + 8, ... with no shared ring and no barrier.
     // K goes straight into registers as MFMA A fragments (two buffers, one block ahead);
-    // V is copied into two private 8 KB LDS stages for the transposed reads.
+    // V is copied into two private 8 KB LDS stages for the transposed reads. Splits are
+    // whole 64-key tiles, so a block never crosses into the next split; past the last key
+    // the loads repeat row T-1, which the mask hides. A block is 16 memory operations (8 K
+    // loads, 8 V copies): waiting for vmcnt(16) after issuing the next block's leaves
+    // exactly this block landed.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     constexpr int VB = 32 * ROWB;  // one V block
     const int nblk = (kend - kbeg + 31) / 32;
