@@ -13,9 +13,9 @@
 //     Key-wave k takes every KSW-th 32-key block of the split with its own online
 //     softmax; the key-waves' partial results are merged in LDS at the end (a tree of
 //     log2 KSW rounds), so small trees and single-token decode still keep two waves busy
-//     on every SIMD. With a single row-wave (bf16 cache) each 32-key block has one
-//     reader, so every wave streams its own blocks (K into registers, V through a private
-//     LDS stage) with no shared ring and no barrier.
+//     on every SIMD. With a single row-wave each 32-key block has one reader, so every
+//     wave streams its own blocks (K into registers, V through a private LDS stage; an
+//     FP8 cache is widened in registers on the way) with no shared ring and no barrier.
 //   * Splits. The key sequence [0, L+N) is cut into S ranges; each workgroup streams one
 //     range for one (KV head, row tile) and writes a normalised fp32 partial output and
 //     its log2-sum-exp. attn_merge_small_kernel (up to 64 splits, one memory round trip)
@@ -571,7 +571,89 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
     }
   };
 
-  if constexpr (kF8) {
+  if constexpr (kF8 && RWV == 1) {
+    // ---- FP8, one row-wave: each wave streams its own 32-key blocks b = wave, wave + 8,
+    // ... with no shared ring and no barrier. K codes come into registers and are widened
+    // there (code * 2^e, the row's exponent, per lane) into the MFMA A fragments; V codes
+    // come into registers, are widened and written to a private 8 KB bf16 stage in the
+    // transposed-read layout. The wave's own LDS accesses stay in order, so one stage
+    // suffices. Codes and exponents of the next block are in flight during this one.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    constexpr int VB = 32 * ROWB;
+    const int nblk = (kend - kbeg + 31) / 32;
+    char* vst = smem + wave * VB;
+    const int32_t* ekp = uniform_ptr(p.ek);
+    const int32_t* evp = uniform_ptr(p.ev);
+    const int vr = lane >> 1, vh = lane & 1;  // V widening: key row vr, codes vh*64 .. +63
+    auto scale_of = [&](int e) __attribute__((always_inline)) -> float {
+      bad_exp |= e < kExpMin || e > kExpMax;
+      e = min(max(e, kExpMin), kExpMax);
+      return __int_as_float((e + 127) << 23);
+    };
+    struct Raw {
+      uint2 k[8];
+      u32x4 v[4];
+      int ek, ev;
+    };
+    auto load_raw = [&](int b, Raw& r) __attribute__((always_inline)) {
+      const int kk = min(kbeg + b * 32 + ql, p.T - 1);
+      const char* krow = kb8 + (uint32_t)kk * rowstride_b + grp * 8;
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8) r.k[s8] = *reinterpret_cast<const uint2*>(krow + s8 * 16);
+      const int kv = min(kbeg + b * 32 + vr, p.T - 1);
+      const char* vrow = vb8 + (uint32_t)kv * rowstride_b + vh * 64;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r.v[j] = *reinterpret_cast<const u32x4*>(vrow + j * 16);
+      r.ek = ekp[(int64_t)kk * p.Hkv + h];
+      r.ev = evp[(int64_t)kv * p.Hkv + h];
+    };
+    auto compute_raw = [&](int b, const Raw& r) __attribute__((always_inline)) {
+      // V: widen and store (after the previous block's transposed reads, in LDS order)
+      const float svv = scale_of(r.ev);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4 lo, hi;
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          lo[2 * q2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.v[j][q2], svv, false));
+          lo[2 * q2 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.v[j][q2], svv, true));
+          hi[2 * q2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.v[j][q2 + 2], svv, false));
+          hi[2 * q2 + 1] =
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.v[j][q2 + 2], svv, true));
+        }
+        const int c = vh * 8 + 2 * j;  // logical 16-byte chunks c, c + 1 of row vr
+        *reinterpret_cast<u32x4*>(vst + vr * ROWB + ((c ^ swz_v(vr)) << 4)) = lo;
+        *reinterpret_cast<u32x4*>(vst + vr * ROWB + (((c + 1) ^ swz_v(vr)) << 4)) = hi;
+      }
+      // K: widen into the A fragments and score
+      const float skk = scale_of(r.ek);
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8) {
+        u32x4 kw;
+        kw[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.k[s8].x, skk, false));
+        kw[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.k[s8].x, skk, true));
+        kw[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.k[s8].y, skk, false));
+        kw[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.k[s8].y, skk, true));
+        acc = mfma32(__builtin_bit_cast(bf16x8, kw), qf[s8], acc);
+      }
+      sc[0] = acc;
+      if (kbeg + b * 32 + 32 > p.L) mask(kbeg + b * 32, 0);
+      softmax(0);
+      pv(vst - VBASE, 0);
+    };
+    Raw r0, r1;
+    int b = wave;
+    if (b < nblk) load_raw(b, r0);
+    for (; b < nblk; b += 16) {
+      if (b + 8 < nblk) load_raw(b + 8, r1);
+      compute_raw(b, r0);
+      if (b + 8 >= nblk) break;
+      if (b + 16 < nblk) load_raw(b + 16, r0);
+      compute_raw(b + 8, r1);
+    }
+    if (__any(bad_exp) && lane == 0 && p.dev_error) *p.dev_error = TV_ERR_INVALID_ARG;
+  } else if constexpr (kF8) {
     // ---- FP8 prologue: raw tiles 0..3 start streaming; 0..2 must land. K of tiles 0, 1
     // and V of tile 0 are widened; the LDS barrier publishes them.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

@@ -212,6 +212,14 @@ def test_fp8_attention_forced_splits(splits):
     _check_fp8_workload(make("budget22", 11, L=7000, N=22), f"splits={splits}", num_splits=splits)
 
 
+# One row-wave: each wave streams and widens its own blocks. T = 5001 keys: the requests
+# give 1, 4, 40 and 79 splits of 158, 40, 4 and 2 blocks, so with few blocks most waves
+# have none, and the last block is cut by the end of the keys.
+@pytest.mark.parametrize("splits", [1, 4, 40, 1024])
+def test_fp8_attention_single_row_wave_splits(splits):
+    _check_fp8_workload(make("decode_1node", 3, L=5000), f"decode splits={splits}", num_splits=splits)
+
+
 def test_fp8_attention_peaky_keys():
     _check_fp8_workload(make("max_256k", 1, L=20000), "peaky 20k")
 
@@ -267,8 +275,10 @@ def test_fp8_attention_strided_cache():
     check_attention(out, ref, label="fp8 strided")
 
 
-def test_fp8_attention_out_of_range_exponent_is_reported():
-    w = make("budget22", 2, L=200)
+# budget22 (88 rows) widens shared tiles; decode (8 rows) widens each wave's own blocks.
+@pytest.mark.parametrize("name", ["budget22", "decode_1node"])
+def test_fp8_attention_out_of_range_exponent_is_reported(name):
+    w = make(name, 2, L=200)
     kc, ke = oracle.quantize_kv(w.k)
     vc, ve = oracle.quantize_kv(w.v)
     for bad_e in (200, -300):
