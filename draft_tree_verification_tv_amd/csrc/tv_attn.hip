@@ -781,10 +781,13 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
       if (t + 1 < ntiles) wait_step(t);
     }
   } else {
-  // ---- prologue: tiles 0, 1, 2 start streaming; tiles 0 and 1 must land.
+  // ---- prologue: tiles 0, 1, 2 start streaming; only tile 0 must land before the first
+  // scores. Step 0 waits for tile 1 (its second block scores tile 1's keys) midway.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // query loads are not tile copies
   for (int t = 0; t < 3 && t < ntiles; ++t) issue(t);
   if (ntiles > 2)
+    barrier_keep<2 * DPT>();
+  else if (ntiles > 1)
     barrier_keep<DPT>();
   else
     barrier_keep<0>();
@@ -807,11 +810,25 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
     wait_step(t);
   };
   int t = 0;
+  if (ntiles > 1) {
+    // Step 0: tile 1 must land before block 1's successor (block 0 of tile 1) is scored.
+    if (3 < ntiles) issue(3);
+    sub(0, B0{}, 0, kstage(0), vstage(0));
+    if (ntiles > 3)
+      barrier_keep<2 * DPT>();
+    else if (ntiles > 2)
+      barrier_keep<DPT>();
+    else
+      barrier_keep<0>();
+    sub(0, B1{}, 1, kstage(1), vstage(0));
+    wait_step(0);
+    t = 1;
+  }
   for (; t + 4 < ntiles; t += 4) {
-    step(t, std::integral_constant<int, 0>{});
-    step(t + 1, std::integral_constant<int, 1>{});
-    step(t + 2, std::integral_constant<int, 2>{});
-    step(t + 3, std::integral_constant<int, 3>{});
+    step(t, std::integral_constant<int, 1>{});
+    step(t + 1, std::integral_constant<int, 2>{});
+    step(t + 2, std::integral_constant<int, 3>{});
+    step(t + 3, std::integral_constant<int, 0>{});
   }
   for (; t + 1 < ntiles; ++t) {
     if (t + 3 < ntiles) issue(t + 3);
