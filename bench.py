@@ -45,10 +45,10 @@ CPU_SAMPLE_SECONDS = 10.0
 # profiles/tv_tree_attn_long_128k_hbm_counters.md. Valid only for the kernel sources they
 # were taken on (compared through a digest of their code without comments): reported as
 # null once that code changes.
-TRAFFIC_BYTES_PER_CALL = 572871419
+TRAFFIC_BYTES_PER_CALL = 572943779
 TRAFFIC_SOURCES = ("draft_tree_verification_tv_amd/csrc/tv_attn.hip",
                    "draft_tree_verification_tv_amd/csrc/tv_internal.h")
-TRAFFIC_SOURCES_SHA256 = "e673aa6eb94ca8cb3eaea3c35a8e067681e1fdfcb28bce46393cb8b0a098b449"
+TRAFFIC_SOURCES_SHA256 = "5f18f04dcc68acd07356f2aaf9690647823aa92b0590974e908c7091fc90c3a5"
 
 
 def code_digest(root, files):
