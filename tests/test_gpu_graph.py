@@ -17,7 +17,7 @@ from workloads import make
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["budget22", "branch_8k"])
+@pytest.mark.parametrize("name", ["budget22", "branch_8k", "decode_1node"])
 def test_graph_replays_match_eager(name):
     w = make(name, 1)
     note(f"graph capture {name}")
