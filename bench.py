@@ -45,10 +45,10 @@ CPU_SAMPLE_SECONDS = 10.0
 # profiles/tv_tree_attn_long_128k_hbm_counters.md. Valid only for the kernel sources they
 # were taken on (compared through a digest of their code without comments): reported as
 # null once that code changes.
-TRAFFIC_BYTES_PER_CALL = 572943779
+TRAFFIC_BYTES_PER_CALL = 572946624
 TRAFFIC_SOURCES = ("draft_tree_verification_tv_amd/csrc/tv_attn.hip",
                    "draft_tree_verification_tv_amd/csrc/tv_internal.h")
-TRAFFIC_SOURCES_SHA256 = "5f18f04dcc68acd07356f2aaf9690647823aa92b0590974e908c7091fc90c3a5"
+TRAFFIC_SOURCES_SHA256 = "4de0eeb636321d0bd949a2a8161240d26e9fe99d6488d0fa680c6cb487fe294c"
 
 
 def code_digest(root, files):

@@ -654,22 +654,23 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
     }
     if (__any(bad_exp) && lane == 0 && p.dev_error) *p.dev_error = TV_ERR_INVALID_ARG;
   } else if constexpr (kF8) {
-    // ---- FP8 prologue: raw tiles 0..3 start streaming; 0..2 must land. K of tiles 0, 1
-    // and V of tile 0 are widened; the LDS barrier publishes them.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // ---- FP8: raw tiles 0..3 start streaming.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // query loads are not tile copies
     for (int t = 0; t < 4 && t < ntiles; ++t) issue(t);
-    if (ntiles > 3)
-      barrier_keep<DPT>();
-    else
-      barrier_keep<0>();
-    widen(0, false);
-    if (ntiles > 1) widen(1, false);
-    widen(0, true);
-    if (ntiles > 3)
-      barrier_keep<DPT>();
-    else
-      barrier_keep<0>();
     if constexpr (KSW > 1) {
+      // Raw tiles 0..2 must land; K of tiles 0, 1 and V of tile 0 are widened and the LDS
+      // barrier publishes them.
+      if (ntiles > 3)
+        barrier_keep<DPT>();
+      else
+        barrier_keep<0>();
+      widen(0, false);
+      if (ntiles > 1) widen(1, false);
+      widen(0, true);
+      if (ntiles > 3)
+        barrier_keep<DPT>();
+      else
+        barrier_keep<0>();
       key_prologue();
       for (int t = 0; t < ntiles; ++t) {
         if (t + 4 < ntiles) issue(t + 4);
@@ -684,6 +685,24 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
         }
       }
     } else {
+    // Only raw tile 0 must land before its K and V are widened; the barrier that publishes
+    // them also waits for raw tile 1.
+    if (ntiles > 3)
+      barrier_keep<3 * DPT>();
+    else if (ntiles > 2)
+      barrier_keep<2 * DPT>();
+    else if (ntiles > 1)
+      barrier_keep<DPT>();
+    else
+      barrier_keep<0>();
+    widen(0, false);
+    widen(0, true);
+    if (ntiles > 3)
+      barrier_keep<2 * DPT>();
+    else if (ntiles > 2)
+      barrier_keep<DPT>();
+    else
+      barrier_keep<0>();
     qk(kstage(0), 0, 0);
     if (nplain == 0) mask(kbeg, 0);
 
@@ -691,7 +710,31 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
     // t-1); K of tile t+2 and V of tile t+1 are widened (their raw tiles landed by the
     // previous barrier; their bf16 stages last held K of tile t-1 and V of tile t-1);
     // tile t is consumed. The barrier guarantees raw tile t+3 and keeps t+4 in flight.
-    for (int t = 0; t + 1 < ntiles; ++t) {
+    // Step 0 is peeled: raw tile 4 goes into the stage of raw tile 0 (widened before the
+    // last barrier), tile 1 is widened first, and a barrier midway publishes it (and
+    // waits for raw tile 2) before the second block scores tile 1's keys; K of tile 2 is
+    // widened last.
+    int t = 0;
+    if (ntiles > 1) {
+      if (4 < ntiles) issue(4);
+      widen(1, false);
+      widen(1, true);
+      sub(0, B0{}, 0, kstage(0), vstage(0));
+      if (ntiles > 4)
+        barrier_keep<2 * DPT>();
+      else if (ntiles > 3)
+        barrier_keep<DPT>();
+      else
+        barrier_keep<0>();
+      sub(0, B1{}, 1, kstage(1), vstage(0));
+      if (2 < ntiles) widen(2, false);
+      if (4 < ntiles)
+        barrier_keep<DPT>();
+      else
+        barrier_keep<0>();
+      t = 1;
+    }
+    for (; t + 1 < ntiles; ++t) {
       if (t + 4 < ntiles) issue(t + 4);
       if (t + 2 < ntiles) widen(t + 2, false);
       widen(t + 1, true);

@@ -220,6 +220,14 @@ def test_fp8_attention_single_row_wave_splits(splits):
     _check_fp8_workload(make("decode_1node", 3, L=5000), f"decode splits={splits}", num_splits=splits)
 
 
+# The 256-row kernel with every short split length (tiles per split 1, 2, 3, 4, 5, 6 and
+# 12): the early start of its prologue widens tile 0 alone, then tile 1 midway through
+# step 0; the raw-tile ring holds four tiles.
+@pytest.mark.parametrize("L,splits", [(700, 12), (700, 6), (700, 4), (700, 3), (700, 2), (700, 1), (1200, 4)])
+def test_fp8_attention_dense_short_splits(L, splits):
+    _check_fp8_workload(make("branch_8k", 4, L=L), f"8x1 L={L} splits={splits}", num_splits=splits)
+
+
 def test_fp8_attention_peaky_keys():
     _check_fp8_workload(make("max_256k", 1, L=20000), "peaky 20k")
 

@@ -267,13 +267,18 @@ def test_attention_single_row_wave_splits(splits):
     check_attention(out, ref, lse, lref, f"decode splits={splits}")
 
 
-# The 256-row kernel (8 row-waves) with every short split length: T = 764 keys, 12 tiles;
-# the requests give splits of 1, 2, 3, 4, 6 and 12 tiles, which exercise the prologue's
-# early start (tile 0 only, then tile 1 midway through step 0) and the unroll's remainder.
-@pytest.mark.parametrize("splits", [12, 6, 4, 3, 2, 1])
-def test_attention_dense_short_splits(splits):
-    w = make("branch_8k", 4, L=700)
-    note(f"attention 8x1 forced splits {splits}")
+# The 256-row kernel (8 row-waves) with every short split length: at L = 700, T = 764
+# keys, 12 tiles, and the requests give splits of 1, 2, 3, 4, 6 and 12 tiles; at L = 1200,
+# T = 1264 keys, 20 tiles, four splits of 5 tiles (the last one cut short). They exercise
+# the prologue's early start (tile 0 only, then tile 1 midway through step 0) and the
+# unroll's remainder.
+DENSE_SHORT = [(700, 12), (700, 6), (700, 4), (700, 3), (700, 2), (700, 1), (1200, 4)]
+
+
+@pytest.mark.parametrize("L,splits", DENSE_SHORT)
+def test_attention_dense_short_splits(L, splits):
+    w = make("branch_8k", 4, L=L)
+    note(f"attention 8x1 L={L} forced splits {splits}")
     out, lse = attn_gpu(w, num_splits=splits)
     ref, lref = attn_ref(w)
     check_attention(out, ref, lse, lref, f"8x1 splits={splits}")
