@@ -17,9 +17,9 @@
 //     wave streams its own blocks (K into registers, V through a private LDS stage; an
 //     FP8 cache is widened in registers on the way) with no shared ring and no barrier.
 //   * Splits. The key sequence [0, L+N) is cut into S ranges; each workgroup streams one
-//     range for one (KV head, row tile) and writes a normalised fp32 partial output and
-//     its log2-sum-exp. attn_merge_small_kernel (up to 64 splits, one memory round trip)
-//     or attn_merge_kernel combines the partials.
+//     range for one (KV head, row tile) and writes a normalised partial output (bf16)
+//     and its log2-sum-exp (fp32). attn_merge_small_kernel (up to 64 splits, one memory
+//     round trip) or attn_merge_kernel combines the partials.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: the
 //     accumulator layout gives every lane one query row (16 keys per 32-key block), so the
 //     online-softmax statistics are lane-local (plus one exchange with lane ^ 32), and
