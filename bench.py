@@ -45,10 +45,10 @@ CPU_SAMPLE_SECONDS = 10.0
 # profiles/tv_tree_attn_long_128k_hbm_counters.md. Valid only for the kernel sources they
 # were taken on (compared through a digest of their code without comments): reported as
 # null once that code changes.
-TRAFFIC_BYTES_PER_CALL = 572934725
+TRAFFIC_BYTES_PER_CALL = 572938003
 TRAFFIC_SOURCES = ("draft_tree_verification_tv_amd/csrc/tv_attn.hip",
                    "draft_tree_verification_tv_amd/csrc/tv_internal.h")
-TRAFFIC_SOURCES_SHA256 = "4de0eeb636321d0bd949a2a8161240d26e9fe99d6488d0fa680c6cb487fe294c"
+TRAFFIC_SOURCES_SHA256 = "f9efc977bcc27b1c9360e59875e52579953917792a866ae444a392bcd7be218f"
 
 
 def code_digest(root, files):

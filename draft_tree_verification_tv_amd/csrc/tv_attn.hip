@@ -737,8 +737,8 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
     for (; t + 1 < ntiles; ++t) {
       if (t + 4 < ntiles) issue(t + 4);
       if (t + 2 < ntiles) widen(t + 2, false);
-      widen(t + 1, true);
       sub(t, B0{}, t, kstage(t), vstage(t));
+      widen(t + 1, true);  // between the blocks, so the two widening bursts are apart
       sub(t, B1{}, t + 1, kstage(t + 1), vstage(t));
       if (t + 4 < ntiles)
         barrier_keep<DPT>();
