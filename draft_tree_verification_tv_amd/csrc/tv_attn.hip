@@ -55,6 +55,7 @@
 //     code * 2^e exactly (v_cvt_scalef32_pk_bf16_fp8), two steps ahead for K and one for
 //     V, inside the same one-barrier-per-tile pipeline. The MFMA and softmax code is
 //     shared with the bf16 kernel, so both compute the same function of the bf16 values.
+#include <atomic>
 #include <cmath>
 
 #include "tv_internal.h"
@@ -773,6 +774,9 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
       const char* row = kb8 + (uint32_t)key * rowstride_b + grp * 16;
 #pragma unroll
       for (int s8 = 0; s8 < 8; ++s8) kf[s8] = *reinterpret_cast<const bf16x8*>(row + s8 * 32);
+      // The stage's previous block was read by transposed LDS reads whose data may not
+      // have returned yet; the copies below overwrite it, so those reads finish first.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int r = 4 * j + (lane >> 4);
@@ -1060,17 +1064,31 @@ __global__ __launch_bounds__(256) void attn_merge_small_kernel(MergeParams mp) {
   if (mp.lse && lane == 0) mp.lse[row] = mx == -INFINITY ? -INFINITY : (mx + __log2f(wsum)) * kLn2;
 }
 
+// The kernels take more than 64 KB of dynamic LDS, which a function attribute must allow
+// on every device before the first launch there. Per kernel, one bit per device records
+// that it was set; the word is atomic, so concurrent first calls from several host threads
+// at worst set the (idempotent) attribute twice. Devices past the 64 bits set it on every
+// call.
+template <typename Kernel>
+hipError_t allow_dynamic_lds(Kernel kernel, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? 1ull << dev : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  done.fetch_or(bit, std::memory_order_release);
+  return hipSuccess;
+}
+
 template <int RWV, bool kF8>
 hipError_t launch_split(const SplitParams& sp, int nwg, hipStream_t stream) {
   constexpr int KSW = 8 / RWV;
   constexpr int smem = kF8 ? F8_SMEM_BYTES : SMEM_BYTES;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_split_kernel<RWV, KSW, kF8>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> attr_devices{0};
+  hipError_t e = allow_dynamic_lds(&attn_split_kernel<RWV, KSW, kF8>, smem, attr_devices);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_split_kernel<RWV, KSW, kF8>), dim3(nwg), dim3(512), smem, stream, sp);
   return hipGetLastError();
 }

@@ -120,6 +120,38 @@ def _need_cuda(name, t, dtype=None):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _need_buf(name, t, dtype, shape=None, min_numel=None, device=None):
+    """A caller-supplied buffer the kernels index as a dense array: dtype, contiguity,
+    device and either an exact shape or a minimum element count are checked before any
+    launch, since a kernel would read or write past a smaller buffer."""
+    _need_cuda(name, t, dtype)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} must hold at least {min_numel} elements, got {t.numel()}")
+
+
+def _opt_buf(name, t, dtype, shape=None, min_numel=None, device=None):
+    if t is not None:
+        _need_buf(name, t, dtype, shape=shape, min_numel=min_numel, device=device)
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _need_workspace(name, t, device):
+    _need_cuda(name, t)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
 def abi_version() -> int:
     return lib().tv_abi_version()
 
@@ -136,7 +168,8 @@ def validate_tree_host(parent) -> int:
 
 def tree_prep(parent, dev_error=None, stream=None):
     """Ancestor bitmasks (int64 [N, 4], bit patterns of uint64 words) and depths int32 [N]."""
-    _need_cuda("parent", parent, torch.int32)
+    _need_buf("parent", parent, torch.int32)
+    _opt_buf("dev_error", dev_error, torch.int32, min_numel=1, device=parent.device)
     n = parent.numel()
     anc = torch.empty((n, 4), dtype=torch.int64, device=parent.device)
     depth = torch.empty(n, dtype=torch.int32, device=parent.device)
@@ -156,7 +189,6 @@ def tree_attn(q, k, v, parent, L=None, scale=None, num_splits=0, out=None, lse=N
     [N, Hq] when given)."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need_cuda(name, t, torch.bfloat16)
-    _need_cuda("parent", parent, torch.int32)
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
         raise ValueError("q, k, v must be 3-D")
     if not q.is_contiguous():
@@ -164,21 +196,31 @@ def tree_attn(q, k, v, parent, L=None, scale=None, num_splits=0, out=None, lse=N
     if k.stride() != v.stride() or k.stride(2) != 1:
         raise ValueError("k and v must share strides with a contiguous last dim")
     N, Hq, D = q.shape
+    dev = q.device
+    if k.device != dev or v.device != dev:
+        raise ValueError("q, k and v must be on one device")
     Hkv = k.shape[1]
+    if k.shape[1:] != (Hkv, D) or v.shape[1:] != (Hkv, D):
+        raise ValueError(f"k and v must be [rows, Hkv, {D}] with one Hkv, got {tuple(k.shape)} and {tuple(v.shape)}")
+    _need_buf("parent", parent, torch.int32, shape=(N,), device=dev)
     if L is None:
         L = k.shape[0] - N
     if L < 0 or k.shape[0] < L + N or v.shape[0] < L + N:
         raise ValueError("k/v must hold L + N rows")
+    _opt_buf("out", out, torch.bfloat16, shape=(N, Hq, D), device=dev)
+    _opt_buf("lse", lse, torch.float32, shape=(N, Hq), device=dev)
+    _opt_buf("dev_error", dev_error, torch.int32, min_numel=1, device=dev)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
-        out = torch.empty((N, Hq, D), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((N, Hq, D), dtype=torch.bfloat16, device=dev)
     if workspace is None:
         ws_bytes = tree_attn_workspace_size(N, L, Hq, Hkv, D, num_splits)
-        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    _need_workspace("workspace", workspace, dev)
     _check(lib().tv_tree_attn(_ptr(q), _ptr(k), _ptr(v), k.stride(0), k.stride(1), _ptr(parent), N, L, Hq,
                               Hkv, D, float(scale), int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace),
-                              workspace.numel() * workspace.element_size(), _ptr(dev_error), _stream(stream)),
+                              _nbytes(workspace), _ptr(dev_error), _stream(stream)),
            "tv_tree_attn")
     return out
 
@@ -197,31 +239,68 @@ def tree_attn_fp8(q, k_codes, v_codes, k_exps, v_exps, parent, L=None, scale=Non
         _need_cuda(name, t, torch.int32)
         if t.dim() != 2 or not t.is_contiguous() or t.shape[1] != k_codes.shape[1]:
             raise ValueError(f"{name} must be a contiguous [T, Hkv] tensor")
-    _need_cuda("parent", parent, torch.int32)
     if q.dim() != 3 or not q.is_contiguous():
         raise ValueError("q must be a contiguous [N, Hq, D] tensor")
     if k_codes.stride() != v_codes.stride() or k_codes.stride(2) != 1:
         raise ValueError("k_codes and v_codes must share strides with a contiguous last dim")
     N, Hq, D = q.shape
+    dev = q.device
+    for t in (k_codes, v_codes, k_exps, v_exps):
+        if t.device != dev:
+            raise ValueError("q, the codes and the exponents must be on one device")
     Hkv = k_codes.shape[1]
+    if k_codes.shape[1:] != (Hkv, D) or v_codes.shape[1:] != (Hkv, D):
+        raise ValueError(f"k_codes and v_codes must be [rows, Hkv, {D}] with one Hkv")
+    if v_exps.shape[1] != Hkv:
+        raise ValueError("v_exps must be a contiguous [T, Hkv] tensor")
+    _need_buf("parent", parent, torch.int32, shape=(N,), device=dev)
     if L is None:
         L = k_codes.shape[0] - N
     rows = L + N
     if L < 0 or min(k_codes.shape[0], v_codes.shape[0], k_exps.shape[0], v_exps.shape[0]) < rows:
         raise ValueError("codes and exponents must hold L + N rows")
+    _opt_buf("out", out, torch.bfloat16, shape=(N, Hq, D), device=dev)
+    _opt_buf("lse", lse, torch.float32, shape=(N, Hq), device=dev)
+    _opt_buf("dev_error", dev_error, torch.int32, min_numel=1, device=dev)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
-        out = torch.empty((N, Hq, D), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((N, Hq, D), dtype=torch.bfloat16, device=dev)
     if workspace is None:
         ws_bytes = tree_attn_workspace_size(N, L, Hq, Hkv, D, num_splits)
-        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    _need_workspace("workspace", workspace, dev)
     _check(lib().tv_tree_attn_fp8(_ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_exps), _ptr(v_exps),
                                   k_codes.stride(0), k_codes.stride(1), _ptr(parent), N, L, Hq, Hkv, D,
                                   float(scale), int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _ptr(dev_error),
-                                  _stream(stream)),
+                                  _nbytes(workspace), _ptr(dev_error), _stream(stream)),
            "tv_tree_attn_fp8")
+    return out
+
+
+def _vocab(logits, V):
+    """Row length to scan: the logits' second dimension unless a shorter V is given."""
+    if V is None:
+        return logits.shape[1]
+    V = int(V)
+    if V < 1 or V > logits.shape[1]:
+        raise ValueError(f"V must lie in [1, {logits.shape[1]}] (the logits' row length), got {V}")
+    return V
+
+
+def _accept_out(out, N, dev):
+    """The four acceptance outputs (accept_len [1], nodes [N], tokens [N], bonus [1] or
+    None), allocated when ``out`` is None, checked otherwise."""
+    if out is None:
+        return (torch.empty(1, dtype=torch.int32, device=dev), torch.empty(N, dtype=torch.int32, device=dev),
+                torch.empty(N, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev))
+    if len(out) != 4:
+        raise ValueError("out must be (accept_len, nodes, tokens, bonus)")
+    ln, nodes, toks, bonus = out
+    _need_buf("accept_len", ln, torch.int32, min_numel=1, device=dev)
+    _need_buf("accept_nodes", nodes, torch.int32, min_numel=N, device=dev)
+    _need_buf("accept_tokens", toks, torch.int32, min_numel=N, device=dev)
+    _opt_buf("bonus", bonus, torch.int32, min_numel=1, device=dev)
     return out
 
 
@@ -242,26 +321,29 @@ def argmax(logits, tok=None, workspace=None, V=None, stream=None):
     if logits.dim() != 2 or logits.stride(1) != 1:
         raise ValueError("logits must be 2-D with a contiguous last dim")
     N = logits.shape[0]
-    V = logits.shape[1] if V is None else V
+    V = _vocab(logits, V)
+    dev = logits.device
+    _opt_buf("tok", tok, torch.int32, shape=(N,), device=dev)
     if tok is None:
-        tok = torch.empty(N, dtype=torch.int32, device=logits.device)
+        tok = torch.empty(N, dtype=torch.int32, device=dev)
     if workspace is None:
-        workspace = argmax_workspace(N, V, logits.device)
+        workspace = argmax_workspace(N, V, dev)
+    _need_workspace("workspace", workspace, dev)
     dt = TV_F32 if logits.dtype == torch.float32 else TV_BF16
     _check(lib().tv_argmax(_ptr(logits), dt, N, V, logits.stride(0), _ptr(tok), _ptr(workspace),
-                           workspace.numel(), _stream(stream)), "tv_argmax")
+                           _nbytes(workspace), _stream(stream)), "tv_argmax")
     return tok
 
 
 def accept(parent, draft, tok, out=None, dev_error=None, stream=None):
     """Longest accepted path. Returns (accept_len [1], nodes [N], tokens [N], bonus [1])."""
-    for name, t in (("parent", parent), ("draft", draft), ("tok", tok)):
-        _need_cuda(name, t, torch.int32)
+    _need_buf("parent", parent, torch.int32)
     N = parent.numel()
-    if out is None:
-        dev = parent.device
-        out = (torch.empty(1, dtype=torch.int32, device=dev), torch.empty(N, dtype=torch.int32, device=dev),
-               torch.empty(N, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev))
+    dev = parent.device
+    _need_buf("draft", draft, torch.int32, shape=(N,), device=dev)
+    _need_buf("tok", tok, torch.int32, shape=(N,), device=dev)
+    _opt_buf("dev_error", dev_error, torch.int32, min_numel=1, device=dev)
+    out = _accept_out(out, N, dev)
     ln, nodes, toks, bonus = out
     _check(lib().tv_accept(_ptr(parent), _ptr(draft), _ptr(tok), N, _ptr(ln), _ptr(nodes), _ptr(toks),
                            _ptr(bonus), _ptr(dev_error), _stream(stream)), "tv_accept")
@@ -274,29 +356,28 @@ def argmax_accept(logits, parent, draft, tok=None, out=None, workspace=None, V=N
 
     Returns (tok [N], (accept_len [1], nodes [N], tokens [N], bonus [1]))."""
     _need_cuda("logits", logits)
-    for name, t in (("parent", parent), ("draft", draft)):
-        _need_cuda(name, t, torch.int32)
     if logits.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("logits must be bf16 or fp32")
     if logits.dim() != 2 or logits.stride(1) != 1:
         raise ValueError("logits must be 2-D with a contiguous last dim")
     N = logits.shape[0]
-    if parent.numel() != N or draft.numel() != N:
-        raise ValueError("parent and draft must have one entry per logits row")
-    V = logits.shape[1] if V is None else V
     dev = logits.device
+    _need_buf("parent", parent, torch.int32, shape=(N,), device=dev)
+    _need_buf("draft", draft, torch.int32, shape=(N,), device=dev)
+    _opt_buf("tok", tok, torch.int32, shape=(N,), device=dev)
+    _opt_buf("dev_error", dev_error, torch.int32, min_numel=1, device=dev)
+    V = _vocab(logits, V)
     if tok is None:
         tok = torch.empty(N, dtype=torch.int32, device=dev)
-    if out is None:
-        out = (torch.empty(1, dtype=torch.int32, device=dev), torch.empty(N, dtype=torch.int32, device=dev),
-               torch.empty(N, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev))
+    out = _accept_out(out, N, dev)
     if workspace is None:
         workspace = argmax_workspace(N, V, dev)
+    _need_workspace("workspace", workspace, dev)
     ln, nodes, toks, bonus = out
     dt = TV_F32 if logits.dtype == torch.float32 else TV_BF16
     _check(lib().tv_argmax_accept(_ptr(logits), dt, N, V, logits.stride(0), _ptr(parent), _ptr(draft), _ptr(tok),
                                   _ptr(ln), _ptr(nodes), _ptr(toks), _ptr(bonus), _ptr(workspace),
-                                  workspace.numel(), _ptr(dev_error), _stream(stream)), "tv_argmax_accept")
+                                  _nbytes(workspace), _ptr(dev_error), _stream(stream)), "tv_argmax_accept")
     return tok, out
 
 
@@ -306,29 +387,28 @@ def sample_accept(logits, parent, draft, temperature, seed, offset=0, tok=None, 
     (Gumbel-max over Philox-4x32-10 keyed by seed, counter offset), then the longest
     accepted path. Returns (tok [N], (accept_len [1], nodes [N], tokens [N], bonus [1]))."""
     _need_cuda("logits", logits)
-    for name, t in (("parent", parent), ("draft", draft)):
-        _need_cuda(name, t, torch.int32)
     if logits.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("logits must be bf16 or fp32")
     if logits.dim() != 2 or logits.stride(1) != 1:
         raise ValueError("logits must be 2-D with a contiguous last dim")
     N = logits.shape[0]
-    if parent.numel() != N or draft.numel() != N:
-        raise ValueError("parent and draft must have one entry per logits row")
-    V = logits.shape[1] if V is None else V
     dev = logits.device
+    _need_buf("parent", parent, torch.int32, shape=(N,), device=dev)
+    _need_buf("draft", draft, torch.int32, shape=(N,), device=dev)
+    _opt_buf("tok", tok, torch.int32, shape=(N,), device=dev)
+    _opt_buf("dev_error", dev_error, torch.int32, min_numel=1, device=dev)
+    V = _vocab(logits, V)
     if tok is None:
         tok = torch.empty(N, dtype=torch.int32, device=dev)
-    if out is None:
-        out = (torch.empty(1, dtype=torch.int32, device=dev), torch.empty(N, dtype=torch.int32, device=dev),
-               torch.empty(N, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev))
+    out = _accept_out(out, N, dev)
     if workspace is None:
         workspace = argmax_workspace(N, V, dev)
+    _need_workspace("workspace", workspace, dev)
     ln, nodes, toks, bonus = out
     dt = TV_F32 if logits.dtype == torch.float32 else TV_BF16
     _check(lib().tv_sample_accept(_ptr(logits), dt, N, V, logits.stride(0), float(temperature), int(seed), int(offset),
                                   _ptr(parent), _ptr(draft), _ptr(tok), _ptr(ln), _ptr(nodes), _ptr(toks),
-                                  _ptr(bonus), _ptr(workspace), workspace.numel(), _ptr(dev_error), _stream(stream)),
+                                  _ptr(bonus), _ptr(workspace), _nbytes(workspace), _ptr(dev_error), _stream(stream)),
            "tv_sample_accept")
     return tok, out
 
@@ -343,10 +423,17 @@ def kv_commit(k, v, L, accept_len, accept_nodes, N=None, new_len=None, dev_error
             raise ValueError(f"{name} must be a 3-D tensor of 2-byte elements")
     if k.stride() != v.stride() or k.stride(2) != 1 or k.shape != v.shape:
         raise ValueError("k and v must share shape and strides with a contiguous last dim")
-    _need_cuda("accept_len", accept_len, torch.int32)
-    _need_cuda("accept_nodes", accept_nodes, torch.int32)
-    N = accept_nodes.numel() if N is None else N
-    if k.shape[0] < L + N:
+    dev = k.device
+    if v.device != dev:
+        raise ValueError("k and v must be on one device")
+    _need_buf("accept_len", accept_len, torch.int32, min_numel=1, device=dev)
+    _need_buf("accept_nodes", accept_nodes, torch.int32, device=dev)
+    N = accept_nodes.numel() if N is None else int(N)
+    if accept_nodes.numel() < N:
+        raise ValueError(f"accept_nodes must hold at least N = {N} entries")
+    _opt_buf("new_len", new_len, torch.int32, min_numel=1, device=dev)
+    _opt_buf("dev_error", dev_error, torch.int32, min_numel=1, device=dev)
+    if L < 0 or k.shape[0] < L + N:
         raise ValueError("k/v must hold L + N rows")
     _check(lib().tv_kv_commit(_ptr(k), _ptr(v), k.stride(0), k.stride(1), k.shape[1], k.shape[2], L, N,
                               _ptr(accept_len), _ptr(accept_nodes), _ptr(new_len), _ptr(dev_error), _stream(stream)),

@@ -35,8 +35,11 @@
  *     that meets an entry outside that range treats it as -1 and, when `dev_error` is
  *     non-NULL, stores TV_ERR_BAD_TREE there (it never writes TV_OK; clear it first).
  *     tv_validate_tree_host() gives the same check synchronously on a host copy.
- *   - No global mutable state: calls on different streams may run concurrently as
- *     long as they do not share output or workspace buffers.
+ *   - Thread safety: calls from any host threads, on different streams, may run
+ *     concurrently as long as they do not share output or workspace buffers. The only
+ *     state kept between calls is per-device information filled in on first use (the
+ *     compute-unit count, whether a kernel's large-LDS launch attribute has been set),
+ *     held in atomics; concurrent first calls at worst repeat that idempotent setup.
  */
 #ifndef TV_H_
 #define TV_H_
