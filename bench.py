@@ -68,6 +68,110 @@ def measured_traffic():
     return TRAFFIC_BYTES_PER_CALL if code_digest(root, TRAFFIC_SOURCES) == TRAFFIC_SOURCES_SHA256 else None
 
 
+def measure_ceilings(K, Vc, T, Hkv, D, layers, stream, attn_call):
+    """Ceilings on this machine, measured with the probe library (include/tv_probe.h):
+
+    * ``hbm_read_gbps``: plain read streams over the layers' K and V caches (HIP events,
+      best of three rounds), read (a) as one contiguous range in 4 KB rows and (b) in the
+      attention call's own pattern -- one KV head's 256-byte rows every Hkv * 256 bytes,
+      one workgroup per (head, key range), K and V caches in turn -- for a few range
+      lengths (``kv_pattern``), and at 32 ranges per head, the attention call's grid of
+      256 workgroups (``kv_pattern_attn_grid``).
+    * ``shader_clock_ghz``: shader-clock cycles over real-time ticks of one spinning wave
+      (rate of the real-time counter measured against HIP events while idle), with the
+      chip idle, during the read stream and during back-to-back attention calls.
+    """
+    import numpy as np
+    import torch
+
+    from draft_tree_verification_tv_amd import probe
+
+    dev = K.device
+    row_b = D * 2
+    nl = min(layers, 8)
+    sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+
+    def timed_bytes(launch, nbytes, rounds=3):
+        launch()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(rounds):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e-3)
+        return nbytes / best / 1e9
+
+    # (a) contiguous: layers 1 .. nl of K, then of V, 4 KB rows
+    span_rows = (nl * T * Hkv * row_b) // 4096
+    contiguous = {}
+    for grid in (512, 1024, 2048):
+        rpw = -(-span_rows // grid)
+
+        def run_contig(rpw=rpw):
+            for buf in (K, Vc):
+                probe.stream_read(buf[1:1 + nl], span_rows, 4096, 4096, 1, rpw, sink)
+        contiguous[grid] = timed_bytes(run_contig, 2 * span_rows * 4096)
+
+    # (b) the KV pattern: column = KV head, rows = keys
+    pattern = {}
+    for ranges in (32, 64, 128):
+        rpw = -(-T // ranges)
+
+        def run_kv(rpw=rpw):
+            for b in range(1, 1 + nl):
+                probe.stream_read(K[b], T, row_b, Hkv * row_b, Hkv, rpw, sink)
+                probe.stream_read(Vc[b], T, row_b, Hkv * row_b, Hkv, rpw, sink)
+        pattern[ranges] = timed_bytes(run_kv, 2 * nl * T * Hkv * row_b)
+
+    # shader clock: the real-time counter's rate first (idle, 20 ms spin)
+    clk = torch.zeros(2, dtype=torch.int64, device=dev)
+    side = torch.cuda.Stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    probe.clock(clk, 2_000_000, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    cyc, ticks = (int(x) for x in clk.cpu())
+    rt_hz = ticks / (e0.elapsed_time(e1) * 1e-3)
+    idle_ghz = cyc / ticks * rt_hz / 1e9
+
+    def clock_under(work_before, work_after, spin_ticks):
+        clk.zero_()
+        torch.cuda.synchronize()
+        work_before()
+        with torch.cuda.stream(side):
+            probe.clock(clk, spin_ticks, side)
+        work_after()
+        torch.cuda.synchronize()
+        c, t = (int(x) for x in clk.cpu())
+        return c / t * rt_hz / 1e9
+
+    ticks_3ms = int(3e-3 * rt_hz)
+    attn_ghz = clock_under(lambda: [attn_call(1 + b % (layers - 1)) for b in range(4)],
+                           lambda: [attn_call(1 + b % (layers - 1)) for b in range(4, 44)], ticks_3ms)
+
+    def kv_reads(n):
+        for i in range(n):
+            b = 1 + i % nl
+            probe.stream_read(K[b], T, row_b, Hkv * row_b, Hkv, -(-T // 64), sink)
+            probe.stream_read(Vc[b], T, row_b, Hkv * row_b, Hkv, -(-T // 64), sink)
+    read_ghz = clock_under(lambda: kv_reads(2), lambda: kv_reads(30), ticks_3ms)
+    del sink
+    return {
+        "hbm_read_gbps": {"contiguous": round(max(contiguous.values()), 1),
+                          "kv_pattern": round(max(pattern.values()), 1),
+                          "kv_pattern_attn_grid": round(pattern[32], 1),
+                          "contiguous_by_grid": {str(k): round(v, 1) for k, v in contiguous.items()},
+                          "kv_pattern_by_ranges_per_head": {str(k): round(v, 1) for k, v in pattern.items()}},
+        "shader_clock_ghz": {"idle": round(idle_ghz, 3), "during_attention": round(attn_ghz, 3),
+                             "during_kv_read_stream": round(read_ghz, 3), "realtime_counter_mhz": round(rt_hz / 1e6, 3)},
+    }
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,6 +354,10 @@ def main():
     copy_gbps = 2 * cp_n / cp_best / 1e9
     del cp_src, cp_dst
 
+    ceilings = measure_ceilings(K, Vc, T, Hkv, D, layers, stream,
+                                lambda b: tv.tree_attn(q, K[b], Vc[b], parent, L=L, scale=w.scale,
+                                                       num_splits=args.splits, out=out, workspace=ws))
+
     # Every attention call timed on its own (steps x layers repetitions): median, p10, p90.
     attn_ms = np.array([e[b].elapsed_time(e[b + 1]) for e in events for b in range(layers)])
     tokens_ms = np.array([e[layers].elapsed_time(e[layers + 1]) for e in events])
@@ -377,6 +485,8 @@ def main():
         "kv_gbps": round(kv_gbps, 1),
         "kv_hbm_frac": round(kv_gbps / HBM_PEAK_GBS, 4),
         "hbm_copy_gbps": round(copy_gbps, 1),
+        "hbm_read_gbps": ceilings["hbm_read_gbps"],
+        "shader_clock_ghz": ceilings["shader_clock_ghz"],
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,

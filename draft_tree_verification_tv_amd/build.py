@@ -19,6 +19,9 @@ INCLUDE = os.path.join(REPO_ROOT, "include")
 LIB_DIR = os.path.join(PKG_DIR, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libtv.so")
 SOURCES = ["tv_api.hip", "tv_attn.hip", "tv_argmax.hip", "tv_tree.hip", "tv_commit.hip", "tv_kvquant.hip"]
+# Measurement probes the benchmark runs beside the library (not part of the verify step).
+PROBE_LIB_PATH = os.path.join(LIB_DIR, "libtv_probe.so")
+PROBE_SOURCES = ["tv_probe.hip"]
 ARCH = "gfx950"
 # Per-file extras. Attention never produces or consumes NaN on valid input (masking uses
 # -inf, which stays honoured), so fmaxf needs no NaN canonicalisation there; the argmax
@@ -51,33 +54,39 @@ def _run(cmd, verbose):
         print(err, file=sys.stderr)
 
 
+def _build_lib(cc, sources, lib_path, tmpdir, verbose):
+    objs, procs = [], []
+    for src in sources:
+        obj = os.path.join(tmpdir, src + ".o")
+        cmd = [cc, *FLAGS, *EXTRA.get(src, []), f"-I{INCLUDE}", "-c", os.path.join(CSRC, src), "-o", obj]
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+        objs.append(obj)
+    for cmd, pr in procs:
+        _, err = pr.communicate()
+        noise = "is not a recognized feature for this target"
+        err = "\n".join(ln for ln in err.splitlines() if noise not in ln)
+        if pr.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({pr.returncode}):\n{' '.join(cmd)}\n{err}")
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+    fd, tmp = tempfile.mkstemp(prefix=os.path.basename(lib_path) + ".", suffix=".so.tmp", dir=LIB_DIR)
+    os.close(fd)
+    try:
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        os.replace(tmp, lib_path)
+    finally:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libtv.so (always recompiles). Returns its path."""
+    """Compile every HIP source and link libtv.so and libtv_probe.so (always recompiles).
+    Returns the path of libtv.so."""
     os.makedirs(LIB_DIR, exist_ok=True)
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="tvbuild.") as tmpdir:
-        objs, procs = [], []
-        for src in SOURCES:
-            obj = os.path.join(tmpdir, src + ".o")
-            cmd = [cc, *FLAGS, *EXTRA.get(src, []), f"-I{INCLUDE}", "-c", os.path.join(CSRC, src), "-o", obj]
-            procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
-            objs.append(obj)
-        for cmd, pr in procs:
-            _, err = pr.communicate()
-            noise = "is not a recognized feature for this target"
-            err = "\n".join(ln for ln in err.splitlines() if noise not in ln)
-            if pr.returncode != 0:
-                raise RuntimeError(f"hipcc failed ({pr.returncode}):\n{' '.join(cmd)}\n{err}")
-            if verbose and err.strip():
-                print(err, file=sys.stderr)
-        fd, tmp = tempfile.mkstemp(prefix="libtv.", suffix=".so.tmp", dir=LIB_DIR)
-        os.close(fd)
-        try:
-            _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-            os.replace(tmp, LIB_PATH)
-        finally:
-            if os.path.exists(tmp):
-                os.unlink(tmp)
+        _build_lib(cc, SOURCES, LIB_PATH, tmpdir, verbose)
+        _build_lib(cc, PROBE_SOURCES, PROBE_LIB_PATH, tmpdir, verbose)
     return LIB_PATH
 
 

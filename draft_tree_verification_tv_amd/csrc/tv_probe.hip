@@ -1,0 +1,97 @@
+// Measurement probes for the benchmark (libtv_probe.so; declarations in include/tv_probe.h).
+// They compute nothing of the verify step: one streams bytes from HBM so that the
+// attention kernel's bandwidth can be set against what a plain read achieves on the same
+// chip and access pattern; the other counts shader clocks against the constant-rate
+// real-time counter to give the clock the chip actually runs at under a given load.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tv_probe.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;  // independent 16-byte loads in flight per thread
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Workgroup w reads rows [w / cols * rows_per_wg, ...) of column w % cols: row r of column
+// c is row_bytes = 2^row_shift bytes at base + r * row_stride + c * row_bytes. Every thread keeps
+// kUnroll 16-byte loads in flight and folds them into an XOR, which the workgroup writes
+// to sink[w] (so no load is dead).
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const char* __restrict__ base, int64_t rows,
+                                                               int row_shift, int64_t row_stride, int cols,
+                                                               int64_t rows_per_wg, uint32_t* __restrict__ sink) {
+  const int w = blockIdx.x;
+  const int col = w % cols;
+  const int64_t r0 = (int64_t)(w / cols) * rows_per_wg;
+  const int64_t r1 = r0 + rows_per_wg < rows ? r0 + rows_per_wg : rows;
+  const int cshift = row_shift - 4;  // 16-byte chunks per row = 2^cshift
+  const int chunks = (int)((r1 - r0) << cshift);
+  const char* cb = base + r0 * row_stride + ((int64_t)col << row_shift);
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int k0 = 0; k0 < chunks; k0 += kThreads * kUnroll) {
+    u32x4 x[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      int k = k0 + u * kThreads + (int)threadIdx.x;
+      if (k >= chunks) k = chunks - 1;  // clamped: every load is in bounds and unconditional
+      x[u] = *reinterpret_cast<const u32x4*>(cb + (int64_t)(k >> cshift) * row_stride + ((k & ((1 << cshift) - 1)) << 4));
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= x[u];
+  }
+  uint32_t v = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  for (int off = 32; off > 0; off >>= 1) v ^= __shfl_xor(v, off);
+  __shared__ uint32_t red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int i = 0; i < kThreads / 64; ++i) r ^= red[i];
+    sink[w] = r;
+  }
+}
+
+// One wave: shader-clock cycles and real-time ticks over a spin of `ticks` real-time ticks.
+// The spin ends when the real-time counter has advanced that far, so it always ends.
+__global__ __launch_bounds__(64) void clock_kernel(uint64_t* __restrict__ out, uint64_t ticks) {
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  uint64_t r1 = r0;
+  while (r1 - r0 < ticks) r1 = __builtin_amdgcn_s_memrealtime();
+  const uint64_t c1 = __builtin_amdgcn_s_memtime();
+  if (threadIdx.x == 0) {
+    out[0] = c1 - c0;
+    out[1] = r1 - r0;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int tv_probe_stream_read(const void* base, int64_t rows, int row_bytes, int64_t row_stride, int cols,
+                         int64_t rows_per_wg, uint32_t* sink, void* stream) {
+  if (!base || !sink || rows < 1 || cols < 1 || rows_per_wg < 1) return 1;
+  int shift = 4;
+  while (shift < 16 && (1 << shift) < row_bytes) ++shift;
+  if (row_bytes != (1 << shift) || row_stride < (int64_t)row_bytes * cols || row_stride % 16 ||
+      (reinterpret_cast<uintptr_t>(base) & 15u))
+    return 1;
+  if ((rows_per_wg << (shift - 4)) > INT32_MAX / 2) return 1;
+  const int64_t groups = (rows + rows_per_wg - 1) / rows_per_wg;
+  if (groups * cols > INT32_MAX) return 1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)(groups * cols)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const char*>(base), rows, shift, row_stride,
+                     cols, rows_per_wg, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+int tv_probe_clock(uint64_t* out, uint64_t ticks, void* stream) {
+  if (!out || ticks < 1 || ticks > 100000000ull) return 1;
+  hipLaunchKernelGGL(clock_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), out, ticks);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+/*
+ * tv_probe.h -- measurement probes that the benchmark runs beside libtv (libtv_probe.so).
+ *
+ * Neither probe is part of the verify step. They give the two ceilings that the attention
+ * kernel's bandwidth is set against on the machine it runs on:
+ *   - the rate at which plain reads stream from HBM, contiguous or in the KV cache's
+ *     pattern (one KV head's 256-byte rows every Hkv * 256 bytes);
+ *   - the shader clock the chip runs at under a given load (it drops below the nominal
+ *     2.4 GHz when power limits bind).
+ * Pointers are device pointers; `stream` is a hipStream_t passed as void*. Both calls
+ * only enqueue work. They return 0 on success, 1 for an invalid argument and 5 when the
+ * HIP runtime refuses the launch.
+ */
+#ifndef TV_PROBE_H_
+#define TV_PROBE_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Streams `rows` x `cols` blocks of `row_bytes` bytes from HBM: block (r, c) lies at
+ * base + r * row_stride + c * row_bytes. Workgroup w (256 threads, each keeping eight
+ * 16-byte loads in flight) reads rows [(w / cols) * rows_per_wg, + rows_per_wg) of column
+ * w % cols; the grid has ceil(rows / rows_per_wg) * cols workgroups. Each workgroup writes
+ * the XOR of what it read to sink[w] (uint32 [grid]), so no load is dead.
+ * Limits: row_bytes a power of two in [16, 65536], row_stride >= row_bytes * cols and a
+ * multiple of 16, base 16-byte aligned, rows_per_wg * row_bytes / 16 below 2^30.
+ */
+int tv_probe_stream_read(const void* base, int64_t rows, int row_bytes, int64_t row_stride, int cols,
+                         int64_t rows_per_wg, uint32_t* sink, void* stream);
+
+/*
+ * One wave spins for `ticks` ticks of the constant-rate real-time counter and writes
+ * out[0] = shader-clock cycles and out[1] = real-time ticks elapsed (uint64 [2]); their
+ * ratio times the real-time rate is the shader clock over the spin. 1 <= ticks <= 1e8.
+ */
+int tv_probe_clock(uint64_t* out, uint64_t ticks, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TV_PROBE_H_ */

@@ -248,3 +248,31 @@ def test_binding_refuses_cpu_tensors():
 ])
 def test_kv_quantize_rejects(args, status):
     assert tv.lib().tv_kv_quantize_fp8(*args, None) == status
+
+
+PROBE_HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "tv_probe.h")
+
+
+def test_probe_library_exports_and_validation():
+    """The benchmark's probe library exports what include/tv_probe.h declares and refuses
+    invalid arguments on the host (status 1) before any launch."""
+    from draft_tree_verification_tv_amd import probe
+    from draft_tree_verification_tv_amd.build import PROBE_LIB_PATH
+
+    if not os.path.exists(PROBE_LIB_PATH):
+        pytest.skip("libtv_probe.so not built")
+    src = open(PROBE_HEADER).read()
+    names = sorted(set(re.findall(r"^\s*\w+\s+(tv_probe_\w+)\s*\(", src, re.M)))
+    assert set(names) == set(probe.EXPORTS)
+    raw = ctypes.CDLL(PROBE_LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    L = probe.lib()
+    sink = FAKE
+    assert L.tv_probe_stream_read(None, 16, 256, 2048, 8, 4, sink, None) == 1          # null buffer
+    assert L.tv_probe_stream_read(FAKE, 16, 384, 4096, 8, 4, sink, None) == 1          # not a power of two
+    assert L.tv_probe_stream_read(FAKE, 16, 256, 1024, 8, 4, sink, None) == 1          # stride below 8 columns
+    assert L.tv_probe_stream_read(ctypes.c_void_p(0x10008), 16, 256, 2048, 8, 4, sink, None) == 1  # misaligned
+    assert L.tv_probe_stream_read(FAKE, 0, 256, 2048, 8, 4, sink, None) == 1           # no rows
+    assert L.tv_probe_clock(None, 100, None) == 1
+    assert L.tv_probe_clock(FAKE, 0, None) == 1
