@@ -8,6 +8,8 @@ from .tv import (  # noqa: F401
     EXPORTS,
     HEAD_DIM,
     MAX_NODES,
+    NOALLOC_SCRATCH_BYTES,
+    TV_ERR_WORKSPACE,
     TVError,
     abi_version,
     accept,
@@ -22,6 +24,7 @@ from .tv import (  # noqa: F401
     status_string,
     tree_attn,
     tree_attn_fp8,
+    tree_attn_noalloc,
     tree_attn_workspace_size,
     tree_prep,
     validate_tree_host,

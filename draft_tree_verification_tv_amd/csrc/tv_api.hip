@@ -35,6 +35,47 @@ bool attn_args_ok(int N, int L, int Hq, int Hkv, int num_splits) {
          (int64_t)Hq * N <= (1 << 24);
 }
 
+// Host checks shared by the bf16-cache attention entry points.
+int attn_bf16_args_status(const void* q, const void* k, const void* v, int64_t kv_stride_t, int64_t kv_stride_h,
+                          const int32_t* parent, int N, int L, int Hq, int Hkv, int D, float scale, int num_splits,
+                          const void* out, const float* lse) {
+  if (!q || !k || !v || !parent || !out) return TV_ERR_INVALID_ARG;
+  if (!attn_args_ok(N, L, Hq, Hkv, num_splits)) return TV_ERR_INVALID_ARG;
+  if (D != TV_HEAD_DIM) return TV_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return TV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return TV_ERR_INVALID_ARG;
+  if (kv_stride_t < 0 || kv_stride_h < 0 || kv_stride_t % 8 || kv_stride_h % 8) return TV_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return TV_ERR_INVALID_ARG;
+  // One KV head's rows must be addressable with 32-bit byte offsets.
+  if (((int64_t)L + N) * kv_stride_t * 2 + 4096 > (int64_t)UINT32_MAX) return TV_ERR_UNSUPPORTED;
+  return TV_OK;
+}
+
+// ---- allocation-free attention: the split partials live in a static device array.
+//
+// `scratch` is a file-scope device array: in host code its name is only a stand-in, so
+// the device address is looked up once per device with hipGetSymbolAddress (with that
+// device current) and kept; kernels receive that address, never the name.
+static __device__ __align__(256) char scratch[TV_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch[kMaxDevices];
+
+hipError_t scratch_on_current_device(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // Concurrent first calls on one device may both look it up; they store the same value.
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -76,20 +117,29 @@ int tv_tree_attn(const void* q, const void* k, const void* v, int64_t kv_stride_
                  const int32_t* parent, int N, int L, int Hq, int Hkv, int D, float scale, int num_splits,
                  void* out, float* lse, void* workspace, size_t workspace_bytes, int32_t* dev_error,
                  void* stream) {
-  if (!q || !k || !v || !parent || !out) return TV_ERR_INVALID_ARG;
-  if (!attn_args_ok(N, L, Hq, Hkv, num_splits)) return TV_ERR_INVALID_ARG;
-  if (D != TV_HEAD_DIM) return TV_ERR_UNSUPPORTED;
-  if (!(scale > 0.f) || !std::isfinite(scale)) return TV_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return TV_ERR_INVALID_ARG;
-  if (kv_stride_t < 0 || kv_stride_h < 0 || kv_stride_t % 8 || kv_stride_h % 8) return TV_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return TV_ERR_INVALID_ARG;
-  // One KV head's rows must be addressable with 32-bit byte offsets.
-  if (((int64_t)L + N) * kv_stride_t * 2 + 4096 > (int64_t)UINT32_MAX) return TV_ERR_UNSUPPORTED;
+  const int st = attn_bf16_args_status(q, k, v, kv_stride_t, kv_stride_h, parent, N, L, Hq, Hkv, D, scale,
+                                       num_splits, out, lse);
+  if (st != TV_OK) return st;
   const tv::AttnPlan p = tv::attn_plan(N, L, Hq, Hkv, num_splits, cu_count());
   const size_t need = tv::attn_workspace_bytes(p, Hkv);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return TV_ERR_WORKSPACE;
   return status_of(tv::launch_tree_attn(p, q, k, v, kv_stride_t, kv_stride_h, parent, N, L, Hq, Hkv, scale, out,
                                         lse, workspace, dev_error, static_cast<hipStream_t>(stream)));
+}
+
+int tv_tree_attn_noalloc(const void* q, const void* k, const void* v, int64_t kv_stride_t, int64_t kv_stride_h,
+                         const int32_t* parent, int N, int L, int Hq, int Hkv, int D, float scale, int num_splits,
+                         void* out, float* lse, int32_t* dev_error, void* stream) {
+  const int st = attn_bf16_args_status(q, k, v, kv_stride_t, kv_stride_h, parent, N, L, Hq, Hkv, D, scale,
+                                       num_splits, out, lse);
+  if (st != TV_OK) return st;
+  const tv::AttnPlan p = tv::attn_plan(N, L, Hq, Hkv, num_splits, cu_count());
+  if (tv::attn_workspace_bytes(p, Hkv) > (size_t)TV_NOALLOC_SCRATCH_BYTES) return TV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const hipError_t e = scratch_on_current_device(&ws);
+  if (e != hipSuccess) return TV_ERR_HIP;
+  return status_of(tv::launch_tree_attn(p, q, k, v, kv_stride_t, kv_stride_h, parent, N, L, Hq, Hkv, scale, out,
+                                        lse, ws, dev_error, static_cast<hipStream_t>(stream)));
 }
 
 int tv_tree_attn_fp8(const void* q, const void* k_codes, const void* v_codes, const int32_t* k_exps,

@@ -26,7 +26,8 @@ HEAD_DIM = 128
 EXPORTS = ("tv_abi_version", "tv_status_string", "tv_validate_tree_host", "tv_tree_prep",
            "tv_tree_attn_workspace_size", "tv_tree_attn", "tv_argmax_workspace_size",
            "tv_argmax", "tv_accept", "tv_argmax_accept", "tv_sample_accept", "tv_kv_commit",
-           "tv_kv_quantize_fp8", "tv_tree_attn_fp8")
+           "tv_kv_quantize_fp8", "tv_tree_attn_fp8", "tv_tree_attn_noalloc")
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class TVError(RuntimeError):
@@ -79,6 +80,9 @@ def lib():
                                        _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]
         L.tv_kv_commit.restype = _i32
         L.tv_kv_commit.argtypes = [_vp, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
+        L.tv_tree_attn_noalloc.restype = _i32
+        L.tv_tree_attn_noalloc.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                           _vp, _vp, _vp, _vp]
         L.tv_tree_attn_fp8.restype = _i32
         L.tv_tree_attn_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
                                        _i32, _vp, _vp, _vp, _sz, _vp, _vp]
@@ -222,6 +226,46 @@ def tree_attn(q, k, v, parent, L=None, scale=None, num_splits=0, out=None, lse=N
                               Hkv, D, float(scale), int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace),
                               _nbytes(workspace), _ptr(dev_error), _stream(stream)),
            "tv_tree_attn")
+    return out
+
+
+def tree_attn_noalloc(q, k, v, parent, L=None, scale=None, num_splits=0, out=None, lse=None, dev_error=None,
+                      stream=None):
+    """tree_attn through the allocation-free entry point: the split partials live in the
+    library's static per-device buffer (NOALLOC_SCRATCH_BYTES), so the C call allocates
+    nothing (pass ``out`` to allocate nothing here either). Calls that can overlap on one
+    device race on that buffer."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need_cuda(name, t, torch.bfloat16)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be 3-D")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if k.stride() != v.stride() or k.stride(2) != 1:
+        raise ValueError("k and v must share strides with a contiguous last dim")
+    N, Hq, D = q.shape
+    dev = q.device
+    if k.device != dev or v.device != dev:
+        raise ValueError("q, k and v must be on one device")
+    Hkv = k.shape[1]
+    if k.shape[1:] != (Hkv, D) or v.shape[1:] != (Hkv, D):
+        raise ValueError(f"k and v must be [rows, Hkv, {D}] with one Hkv, got {tuple(k.shape)} and {tuple(v.shape)}")
+    _need_buf("parent", parent, torch.int32, shape=(N,), device=dev)
+    if L is None:
+        L = k.shape[0] - N
+    if L < 0 or k.shape[0] < L + N or v.shape[0] < L + N:
+        raise ValueError("k/v must hold L + N rows")
+    _opt_buf("out", out, torch.bfloat16, shape=(N, Hq, D), device=dev)
+    _opt_buf("lse", lse, torch.float32, shape=(N, Hq), device=dev)
+    _opt_buf("dev_error", dev_error, torch.int32, min_numel=1, device=dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((N, Hq, D), dtype=torch.bfloat16, device=dev)
+    _check(lib().tv_tree_attn_noalloc(_ptr(q), _ptr(k), _ptr(v), k.stride(0), k.stride(1), _ptr(parent), N, L, Hq,
+                                      Hkv, D, float(scale), int(num_splits), _ptr(out), _ptr(lse), _ptr(dev_error),
+                                      _stream(stream)),
+           "tv_tree_attn_noalloc")
     return out
 
 

@@ -122,6 +122,26 @@ int tv_tree_attn(const void* q, const void* k, const void* v, int64_t kv_stride_
                  void* stream);
 
 /*
+ * Tree attention that allocates nothing, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, results and limits are those of tv_tree_attn without the workspace (the same
+ * kernels, so the same outputs bit for bit). The split partials go to a static device
+ * buffer of TV_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on
+ * until the process ends; the call itself allocates nothing. A call whose partials need
+ * more (tv_tree_attn_workspace_size(...) > TV_NOALLOC_SCRATCH_BYTES, e.g. forced split
+ * counts far above the default) returns TV_ERR_WORKSPACE and enqueues nothing. Every call
+ * on one device shares that device's buffer: calls that can overlap on one device (other
+ * streams, other host threads) race on it and must be ordered by the caller. The buffer
+ * needs no initialisation (each call writes every partial it reads).
+ */
+#define TV_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int tv_tree_attn_noalloc(const void* q, const void* k, const void* v, int64_t kv_stride_t,
+                         int64_t kv_stride_h, const int32_t* parent, int N, int L, int Hq,
+                         int Hkv, int D, float scale, int num_splits, void* out, float* lse,
+                         int32_t* dev_error, void* stream);
+
+/*
  * Tree attention over an FP8 key/value cache (the quantised cache of Lucebox-Hub review,
  * section "2. DFlash"; format of tv_kv_quantize_fp8). Computes tv_tree_attn on the
  * dequantised cache k[t][h][d] = decode(k_codes[t][h][d]) * 2^k_exps[t * Hkv + h] (and

@@ -276,3 +276,22 @@ def test_probe_library_exports_and_validation():
     assert L.tv_probe_stream_read(FAKE, 0, 256, 2048, 8, 4, sink, None) == 1           # no rows
     assert L.tv_probe_clock(None, 100, None) == 1
     assert L.tv_probe_clock(FAKE, 0, None) == 1
+
+
+def noalloc_call(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, st=1024, sh=128, parent=FAKE, N=4, L=100, Hq=8, Hkv=2, D=128,
+             scale=0.088, splits=0, out=FAKE, lse=None, err=None, stream=None)
+    a.update(kw)
+    return tv.lib().tv_tree_attn_noalloc(a["q"], a["k"], a["v"], a["st"], a["sh"], a["parent"], a["N"], a["L"],
+                                         a["Hq"], a["Hkv"], a["D"], a["scale"], a["splits"], a["out"], a["lse"],
+                                         a["err"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(out=None), 1), (dict(N=0), 1), (dict(D=64), 3), (dict(scale=0.0), 1),
+    (dict(st=1001), 1), (dict(q=ctypes.c_void_p(0x10002)), 1),
+    # partials beyond the static buffer (8 KV heads x 1024 splits at 128K keys): refused
+    (dict(L=131072, st=1024, Hq=32, Hkv=8, splits=1024), 4),
+])
+def test_tree_attn_noalloc_rejects(kw, status):
+    assert noalloc_call(**kw) == status
