@@ -960,6 +960,270 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
   }
 }
 
+// ---- At most 16 stacked rows (single-token decode, small trees): 16x16x32 MFMA tiles.
+//
+// A 32-row tile would leave at least half of every MFMA and of the softmax work on empty
+// rows here; 16-row tiles (v_mfma_f32_16x16x32_bf16) halve both. The memory side is the
+// single-row-wave stream of attn_split_kernel: each of the eight waves streams its own
+// 32-key blocks (K straight into registers as MFMA A fragments, V through two private LDS
+// stages for the transposed reads), one block ahead, with no shared ring and no barrier.
+// The query, and for the split that reaches the tree the parent entries, are loaded
+// together with the first key block, so their round trips overlap.
+//
+// Layouts. Scores S^T = K Q^T per 16-key half: lane l holds keys 4(l/16) + i (i < 4) of
+// query row l % 16, so a row's 32 keys sit in four lanes (l, l^16, l^32, l^48). The P.V
+// product O^T += V^T P^T takes each lane's own eight probabilities as its B fragment, the
+// reduction order of the 32 keys being (4g .. 4g+3, 16+4g .. 16+4g+3) for lane group g;
+// two transposed LDS reads give the V^T A fragment in that same order. O^T accumulates in
+// 8 x 4 fp32 registers per lane (dims 16 db + 4 g + i of row l % 16).
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// V swizzle of the 16-row kernel: chunk c of key row r lives at chunk c ^ 2(r & 7). A
+// half-wave of transposed reads touches rows r0 .. r0 + 7 and the two chunks of one
+// 16-dim column block, which this maps onto all 16 chunks (all 64 banks) once.
+__device__ __forceinline__ int swz_v16(int r) { return (r & 7) << 1; }
+
+constexpr int R16_STAGES = 2;
+constexpr int R16_VB = 32 * ROWB;                    // one 32-key V block, 8 KB
+constexpr int R16_TREE_OFF = 8 * R16_STAGES * R16_VB;
+constexpr int R16_SMEM_BYTES = R16_TREE_OFF + TREE_BYTES;
+static_assert(R16_SMEM_BYTES <= 160 * 1024, "16-row kernel LDS");
+
+__global__ __launch_bounds__(512) void attn_rows16_kernel(SplitParams p) {
+  constexpr int NW = 8;
+  extern __shared__ __align__(16) char smem[];
+  uint64_t* anc = reinterpret_cast<uint64_t*>(smem + R16_TREE_OFF);
+  int* par = reinterpret_cast<int*>(smem + R16_TREE_OFF + TREE_ANC_BYTES);
+  int* jmp = par + kMaxNodes;
+
+  // ---- work item (RT == 1: one row tile)
+  int w = blockIdx.x;
+  if (p.remap) {
+    const int per = gridDim.x >> 3;
+    w = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  }
+  const int s = w % p.S;
+  const int h = w / p.S;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int i16 = lane & 15;
+  const int g = lane >> 4;
+  const bool rvalid = i16 < p.M;
+  const int node = rvalid ? i16 / p.G : 0;
+  const int qh = h * p.G + (rvalid ? i16 % p.G : 0);
+
+  const int kbeg = s * p.KS;
+  const int kend = min(kbeg + p.KS, p.T);
+  const bool tree = kend > p.L;  // uniform over the workgroup
+  const int nblk = (kend - kbeg + 31) / 32;
+
+  // ---- loads whose round trips overlap the first key block: parent entries, query
+  const int parent_i = (tree && tid < p.N) ? p.parent[tid] : -1;
+  bf16x8 qf[4];  // B fragments of S^T: row i16, dims 32c + 8g .. + 7
+  {
+    const uint16_t* qrow = p.q + ((int64_t)node * p.Hq + qh) * D + g * 8;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (rvalid) x = *reinterpret_cast<const u32x4*>(qrow + c * 32);
+      qf[c] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  const char* kb8 = static_cast<const char*>(p.k) + (int64_t)h * p.sh * 2;
+  const char* vb8 = static_cast<const char*>(p.v) + (int64_t)h * p.sh * 2;
+  const uint32_t rowstride_b = (uint32_t)p.st * 2u;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
+  const uint32_t vpriv = lds_base + (uint32_t)(wave * R16_STAGES * R16_VB);
+  const char* vprivp = smem + wave * R16_STAGES * R16_VB;
+  // transposed-read offsets: key row 4g + i16/4 (the second read adds 16 rows), 8-byte
+  // piece i16 % 4 of the 32-byte span of dims 16 db .. 16 db + 15
+  int voff[8];
+  {
+    const int row = 4 * g + (i16 >> 2);
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      voff[db] = row * ROWB + (((2 * db + ((i16 & 3) >> 1)) ^ swz_v16(row)) << 4) + (i16 & 1) * 8;
+  }
+
+  // One 32-key block: 8 K fragment loads (keys 16 hh + i16, dims 32 c + 8 g) and 8 V copies
+  // of 4 rows each (lane -> row 4 j + lane / 16, physical chunk lane % 16, which holds
+  // logical chunk (lane % 16) ^ swz_v16(row)). Keys past T - 1 repeat row T - 1 (masked).
+  // 16 memory operations per block.
+  auto load_block = [&](int b, bf16x8(&kf)[8], int stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int key = min(kbeg + b * 32 + 16 * hh + i16, p.T - 1);
+      const char* row = kb8 + (uint32_t)key * rowstride_b + g * 16;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kf[4 * hh + c] = *reinterpret_cast<const bf16x8*>(row + c * 64);
+    }
+    // the stage's previous block was read by transposed LDS reads; they finish first
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 4 * j + (lane >> 4);
+      const int pc = lane & 15;
+      const uint32_t grow = (uint32_t)min(kbeg + b * 32 + r, p.T - 1) * rowstride_b;
+      dma16(vpriv + (uint32_t)(stage * R16_VB + j * 1024), grow + (uint32_t)((pc ^ swz_v16(r)) << 4), vb8);
+    }
+  };
+
+  f32x4 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = f32x4{};
+  float m_ref = -INFINITY;  // reference maximum of the row (log2 domain, scaled), equal in its four lanes
+  float lsum = 0.f;         // this lane's part of the row sum relative to m_ref
+  bf16x8 pb;                // P^T fragment of the current block
+
+  // probabilities against the reference (0 while unset); returns the lane's fp32 sum
+  auto probs = [&](const float (&sc)[8]) __attribute__((always_inline)) -> float {
+    const float mu = m_ref == -INFINITY ? 0.f : m_ref;
+    float bs = 0.f;
+    bf16x2 b2[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * j], p.c, -mu));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * j + 1], p.c, -mu));
+      b2[j] = __builtin_convertvector((f32x2{p0, p1}), bf16x2);
+      bs += p0 + p1;
+    }
+    pb = bf16x8{b2[0][0], b2[0][1], b2[1][0], b2[1][1], b2[2][0], b2[2][1], b2[3][0], b2[3][1]};
+    return bs;
+  };
+
+  auto compute_block = [&](int b, const bf16x8(&kf)[8], int stage) __attribute__((always_inline)) {
+    f32x4 s0 = f32x4{}, s1 = f32x4{};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      s0 = mfma16(kf[c], qf[c], s0);
+      s1 = mfma16(kf[4 + c], qf[c], s1);
+    }
+    float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    const int kb0 = kbeg + b * 32;
+    if (kb0 + 32 > p.L) {
+      // 32-bit window of the row's ancestor set: bit bb <-> key kb0 + bb (context keys set)
+      const int d = kb0 - p.L;
+      const uint64_t* a = anc + node * kAncWords;
+      uint32_t win;
+      if (d >= 0) {
+        const int wi = d >> 6, sh = d & 63;
+        const uint64_t lo = wi < kAncWords ? a[wi] : 0ull;
+        const uint64_t hi = (sh > 32 && wi + 1 < kAncWords) ? a[wi + 1] : 0ull;
+        win = (uint32_t)((lo >> sh) | (sh > 32 ? hi << (64 - sh) : 0ull));
+      } else {
+        win = (uint32_t)((a[0] << (-d)) | ((1ull << (-d)) - 1ull));
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int bb = 16 * (e >> 2) + 4 * g + (e & 3);
+        if (!((win >> bb) & 1u)) sc[e] = -INFINITY;
+      }
+    }
+    // online softmax with the lazy reference of attn_split_kernel: the exact path (row
+    // maximum over the four lanes of the row, rescale) only when some lane's block sum
+    // exceeds 2^8 or the reference is unset
+    float bs = probs(sc);
+    const bool need = m_ref == -INFINITY || bs > kCheck;
+    if (__any(need)) {
+      float m = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+#pragma unroll
+      for (int e = 3; e < 7; e += 2) m = fmaxf(fmaxf(m, sc[e]), sc[e + 1]);
+      m = fmaxf(m, sc[7]);
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      const float m_new = fmaxf(m_ref, m * p.c);
+      const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new);
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] *= alpha;
+      m_ref = m_new;
+      bs = probs(sc);
+    }
+    lsum += bs;
+    const char* Vs = vprivp + stage * R16_VB;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + voff[db]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + voff[db] + 16 * ROWB));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[db] = mfma16(a, pb, o[db]);
+    }
+  };
+
+  bf16x8 kf0[8], kf1[8];
+  int b = wave;
+  if (b < nblk) load_block(b, kf0, 0);
+  if (tree) tree_prep_lds_from(parent_i, p.N, anc, par, jmp, p.dev_error);
+  // Block b + 8's 16 operations are issued before block b's are awaited: vmcnt(16) leaves
+  // exactly them in flight (older loads, the query's included, have landed by then).
+  for (; b < nblk; b += 16) {
+    if (b + 8 < nblk) {
+      load_block(b + 8, kf1, 1);
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    compute_block(b, kf0, 0);
+    if (b + 8 >= nblk) break;
+    if (b + 16 < nblk) {
+      load_block(b + 16, kf0, 0);
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    compute_block(b + 8, kf1, 1);
+  }
+
+  // ---- the eight waves' states meet in LDS (the V stages are free after the barrier):
+  // each wave leaves O (16 rows x 128 dims, row pitch 132 floats), its references and its
+  // row sums; then wave w combines rows 2w and 2w + 1 (lane -> row 2w + lane / 32, dims
+  // 4 (lane % 32) .. + 3) and writes the split's normalised partial output.
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  constexpr int OP = 132;
+  constexpr int WSLOT = 16 * OP + 32;
+  float* ms = reinterpret_cast<float*>(smem);
+  barrier_keep<0>();
+  {
+    float* mine = ms + wave * WSLOT;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(mine + i16 * OP + 16 * db + 4 * g) = o[db];
+    if (g == 0) {
+      mine[16 * OP + i16] = m_ref;
+      mine[16 * OP + 16 + i16] = lsum;
+    }
+  }
+  barrier_keep<0>();
+  const int orow = 2 * wave + (lane >> 5);
+  const int od = 4 * (lane & 31);
+  float mk[NW];
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    mk[k] = ms[k * WSLOT + 16 * OP + orow];
+    M = fmaxf(M, mk[k]);
+  }
+  float L = 0.f;
+  f32x4 acc = f32x4{};
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    const float a = mk[k] == -INFINITY ? 0.f : exp2f(mk[k] - M);
+    L += a * ms[k * WSLOT + 16 * OP + 16 + orow];
+    acc += a * *reinterpret_cast<const f32x4*>(ms + k * WSLOT + orow * OP + od);
+  }
+  if (orow < p.M) {
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const int64_t base = ((int64_t)h * p.RT * p.S + s) * TILE_ROWS + orow;
+    *reinterpret_cast<bf16x4*>(p.part_o + base * D + od) = __builtin_convertvector(acc * inv, bf16x4);
+    if ((lane & 31) == 0) p.part_lse[base] = L > 0.f ? M + __log2f(L) : -INFINITY;
+  }
+}
+
 struct MergeParams {
   const __bf16* part_o;
   const float* part_lse;
@@ -1169,7 +1433,14 @@ hipError_t launch_attn(const AttnPlan& plan, bool f8, const void* q, const void*
   sp.remap = (nwg % 8 == 0) ? 1 : 0;
 
   hipError_t e;
-  if (f8) {
+  if (!f8 && plan.M <= 16) {
+    static std::atomic<uint64_t> attr_devices{0};
+    e = allow_dynamic_lds(&attn_rows16_kernel, R16_SMEM_BYTES, attr_devices);
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL(attn_rows16_kernel, dim3(nwg), dim3(512), R16_SMEM_BYTES, stream, sp);
+      e = hipGetLastError();
+    }
+  } else if (f8) {
     switch (plan.RWV) {
       case 1: e = launch_split<1, true>(sp, nwg, stream); break;
       case 2: e = launch_split<2, true>(sp, nwg, stream); break;

@@ -267,6 +267,31 @@ def test_attention_single_row_wave_splits(splits):
     check_attention(out, ref, lse, lref, f"decode splits={splits}")
 
 
+# At most 16 stacked rows (N * G <= 16): the 16x16-tile kernel. The shapes fill the tile
+# exactly (16 x 1, 4 x 4, 2 x 8 rows) or partly, put tree keys in the last block (chains,
+# random trees, a pure tree with L = 0, ragged lengths) and, with peaky keys, move the
+# lazy softmax reference often.
+ROWS16 = [
+    ("chain16_G1", dict(L=1000, N=16, tree="chain", Hq=8, Hkv=8)),
+    ("N4_G4", dict(L=2500, N=4, tree="random16", Hq=16, Hkv=4)),
+    ("N2_G8_L0", dict(L=0, N=2, tree="chain", Hq=8, Hkv=1)),
+    ("N11_G1_L31", dict(L=31, N=11, tree="random16", Hq=3, Hkv=3)),
+    ("N3_G5_L96", dict(L=96, N=3, tree="random16", Hq=10, Hkv=2)),
+    ("N1_G8_peaky", dict(L=20000, N=1, tree="chain", Hq=8, Hkv=1, peaky=True)),
+    ("N2_G6_peaky", dict(L=9000, N=2, tree="chain", Hq=24, Hkv=4, peaky=True)),
+]
+
+
+@pytest.mark.parametrize("label,ov", ROWS16, ids=[e[0] for e in ROWS16])
+def test_attention_rows16(label, ov):
+    w = make("budget22", 13, **ov)
+    assert w.N * w.Hq // w.Hkv <= 16
+    note(f"attention 16-row {label}")
+    out, lse = attn_gpu(w)
+    ref, lref = attn_ref(w)
+    check_attention(out, ref, lse, lref, label)
+
+
 # The 256-row kernel (8 row-waves) with every short split length: at L = 700, T = 764
 # keys, 12 tiles, and the requests give splits of 1, 2, 3, 4, 6 and 12 tiles; at L = 1200,
 # T = 1264 keys, 20 tiles, four splits of 5 tiles (the last one cut short). They exercise
