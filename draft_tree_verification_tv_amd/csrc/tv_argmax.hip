@@ -7,11 +7,18 @@
 //      loads (addresses clamped into the slice, so no load is conditional and all four
 //      are in flight together), keeps only a per-vector max and one compare, and looks up
 //      the element index once, in the winning vector that is still in registers. The
-//      workgroup's (value, index) goes to the workspace (or straight to tok when a row
-//      is a single slice).
-//   2. argmax_final: one wave per row reduces that row's slices.
-// The kernel boundary orders the two, so no atomics, fences or counters are needed and
-// the workspace needs no initialisation.
+//      workgroup's (value, index) goes to the workspace as one 64-bit ordered key (or
+//      straight to tok when a row is a single slice).
+//   2. argmax_final (one wave per row) or, for tv_argmax_accept, argmax_accept_kernel
+//      (one workgroup: the largest key of every row, then the acceptance walk).
+// The key orders (value, index) so that the largest key is the row maximum at its lowest
+// index: the high word is the value's bits mapped to an unsigned order (-0.0 first made
+// +0.0, so the two tie as floats do), the low word the complement of the index. The kernel
+// boundary orders the two launches, so no atomics, fences or counters are needed and the
+// workspace needs no initialisation. A one-launch form, in which each workgroup folds its
+// key into the row's with an atomic maximum and the workgroup completing the last row
+// walks the tree, was measured slower: its chain of device-scope atomics takes longer than
+// the kernel boundary.
 #include <climits>
 #include <cmath>
 
@@ -66,19 +73,13 @@ __device__ __forceinline__ float load_one(const char* row, int e) {
   return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[e] << 16);
 }
 
+// This thread's best (value, index) over its part of elements [begin, end) of the row at
+// rp; {-inf, INT_MAX} when it has no element.
 template <bool kF32, bool kVec>
-__global__ __launch_bounds__(kBlock) void argmax_partial(const char* __restrict__ logits, int V, int64_t row_bytes,
-                                                         int chunks, int chunk_len, int32_t* __restrict__ tok,
-                                                         float* __restrict__ part_v, int* __restrict__ part_i) {
+__device__ __forceinline__ Best slice_scan(const char* __restrict__ rp, int begin, int end) {
   constexpr int EPV = kVec ? (kF32 ? 4 : 8) : 1;  // elements per 16-byte load
   constexpr int ESZ = kF32 ? 4 : 2;
-  const int row = blockIdx.y;
-  const int c = blockIdx.x;
-  const char* rp = logits + (int64_t)row * row_bytes;
-  const int begin = c * chunk_len;
-  const int end = min(V, begin + chunk_len);
   const int tid = threadIdx.x;
-
   Best b{-INFINITY, INT_MAX};
   bool have = false;
   if constexpr (kVec) {
@@ -145,38 +146,77 @@ __global__ __launch_bounds__(kBlock) void argmax_partial(const char* __restrict_
   }
   if (!have) b = Best{-INFINITY, INT_MAX};
 
+  return b;
+}
+
+// Workgroup reduction of slice_scan results; the result is valid in thread 0.
+__device__ __forceinline__ Best block_best(Best b) {
   __shared__ float sv[kBlock / 64];
   __shared__ int si[kBlock / 64];
   b = wave_reduce(b);
-  const int wave = tid >> 6;
-  if ((tid & 63) == 0) {
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
     sv[wave] = b.v;
     si[wave] = b.i;
   }
   __syncthreads();
-  if (tid == 0) {
-    Best r{sv[0], si[0]};
-    for (int w = 1; w < kBlock / 64; ++w) r = better(r, Best{sv[w], si[w]});
-    if (chunks == 1) {
+  Best r{sv[0], si[0]};
+  for (int w = 1; w < kBlock / 64; ++w) r = better(r, Best{sv[w], si[w]});
+  return r;
+}
+
+// 64-bit key ordering (value, index) as described at the top of the file.
+__device__ __forceinline__ uint64_t order_key(Best b) {
+  const float v = b.v == 0.f ? 0.f : b.v;
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)b.i;
+}
+
+// The token a row's largest key stands for (-1 for a row without elements).
+__device__ __forceinline__ int32_t key_token(uint64_t key) {
+  const uint32_t idx = ~(uint32_t)key;
+  return (key == 0ull || idx == (uint32_t)INT_MAX) ? -1 : (int32_t)idx;
+}
+
+// Thread 0 stores the workgroup result of slice c of row `row`.
+__device__ __forceinline__ void store_slice(Best r, int row, int c, int chunks, int32_t* __restrict__ tok,
+                                            uint64_t* __restrict__ part) {
+  if (threadIdx.x == 0) {
+    if (chunks == 1)
       tok[row] = r.i == INT_MAX ? -1 : r.i;
-    } else {
-      part_v[(int64_t)row * chunks + c] = r.v;
-      part_i[(int64_t)row * chunks + c] = r.i;
-    }
+    else
+      part[(int64_t)row * chunks + c] = order_key(r);
   }
 }
 
-// One wave per row: reduce the row's slice results.
-__global__ __launch_bounds__(256) void argmax_final(int N, int chunks, const float* __restrict__ part_v,
-                                                    const int* __restrict__ part_i, int32_t* __restrict__ tok) {
+template <bool kF32, bool kVec>
+__global__ __launch_bounds__(kBlock) void argmax_partial(const char* __restrict__ logits, int V, int64_t row_bytes,
+                                                         int chunks, int chunk_len, int32_t* __restrict__ tok,
+                                                         uint64_t* __restrict__ part) {
+  const int row = blockIdx.y;
+  const int c = blockIdx.x;
+  const char* rp = logits + (int64_t)row * row_bytes;
+  const int begin = c * chunk_len;
+  store_slice(block_best(slice_scan<kF32, kVec>(rp, begin, min(V, begin + chunk_len))), row, c, chunks, tok, part);
+}
+
+// One wave per row: the row's largest slice key.
+__global__ __launch_bounds__(256) void argmax_final(int N, int chunks, const uint64_t* __restrict__ part,
+                                                    int32_t* __restrict__ tok) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= N) return;
-  Best r{-INFINITY, INT_MAX};
-  for (int j = lane; j < chunks; j += 64)
-    r = better(r, Best{part_v[(int64_t)row * chunks + j], part_i[(int64_t)row * chunks + j]});
-  r = wave_reduce(r);
-  if (lane == 0) tok[row] = r.i == INT_MAX ? -1 : r.i;
+  uint64_t k = 0;
+  for (int j = lane; j < chunks; j += 64) {
+    const uint64_t x = part[(int64_t)row * chunks + j];
+    k = x > k ? x : k;
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint64_t o = __shfl_xor(k, off);
+    k = o > k ? o : k;
+  }
+  if (lane == 0) tok[row] = key_token(k);
 }
 
 // ---- sampled targets (temperature > 0)
@@ -221,21 +261,15 @@ __device__ __forceinline__ float gumbel_score(float x, uint32_t word, float c) {
 // Grid (slices, rows), 256 threads; the slice layout and outputs are those of
 // argmax_partial. Each thread scores eight consecutive entries per step (two Philox
 // blocks); a row that is not 16-byte aligned is read element by element.
+// This thread's best (Gumbel score, index) over its entries of [begin, end) of row `row`.
+// Entries [e, e + 8): e is a multiple of 8 relative to the row, so the two Philox blocks
+// are (e / 4) and (e / 4 + 1).
 template <bool kF32, bool kVec>
-__global__ __launch_bounds__(kBlock) void sample_partial(const char* __restrict__ logits, int V, int64_t row_bytes,
-                                                         int chunks, int chunk_len, SampleKey key,
-                                                         int32_t* __restrict__ tok, float* __restrict__ part_v,
-                                                         int* __restrict__ part_i) {
+__device__ __forceinline__ Best sample_scan(const char* __restrict__ rp, int begin, int end, int row,
+                                            const SampleKey& key) {
   constexpr int ESZ = kF32 ? 4 : 2;
-  const int row = blockIdx.y;
-  const int c = blockIdx.x;
-  const char* rp = logits + (int64_t)row * row_bytes;
-  const int begin = c * chunk_len;
-  const int end = min(V, begin + chunk_len);
   const int tid = threadIdx.x;
   Best b{-INFINITY, INT_MAX};
-  // Entries [e, e + 8): e is a multiple of 8 relative to the row, so the two Philox blocks
-  // are (e / 4) and (e / 4 + 1).
   for (int e = begin + tid * 8; e < end; e += kBlock * 8) {
     float x[8];
     if (kVec && e + 8 <= end) {
@@ -273,83 +307,63 @@ __global__ __launch_bounds__(kBlock) void sample_partial(const char* __restrict_
     }
   }
 
-  __shared__ float sv[kBlock / 64];
-  __shared__ int si[kBlock / 64];
-  b = wave_reduce(b);
-  const int wave = tid >> 6;
-  if ((tid & 63) == 0) {
-    sv[wave] = b.v;
-    si[wave] = b.i;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    Best r{sv[0], si[0]};
-    for (int w = 1; w < kBlock / 64; ++w) r = better(r, Best{sv[w], si[w]});
-    if (chunks == 1) {
-      tok[row] = r.i == INT_MAX ? -1 : r.i;
-    } else {
-      part_v[(int64_t)row * chunks + c] = r.v;
-      part_i[(int64_t)row * chunks + c] = r.i;
-    }
-  }
+  return b;
 }
 
-// One workgroup finishes the verify step: thread i reduces node row i's slice results to
-// the row argmax (loads batched 32 slices at a time, one round trip for vocabularies up to
-// 262144 bf16 entries; indices clamped so that no load is conditional, and a repeated
-// (value, index) pair cannot change the result), keeps the tokens
-// in LDS and runs the acceptance walk on them (the walk of tv_accept). The draft and
-// parent entries and the first batch of slice results are loaded together, ahead of the
-// tree preprocessing, so that their round trips overlap. With a single slice per row the
-// slice kernel already wrote tok.
-constexpr int kFuseThreads = kMaxNodes;
+template <bool kF32, bool kVec>
+__global__ __launch_bounds__(kBlock) void sample_partial(const char* __restrict__ logits, int V, int64_t row_bytes,
+                                                         int chunks, int chunk_len, SampleKey key,
+                                                         int32_t* __restrict__ tok, uint64_t* __restrict__ part) {
+  const int row = blockIdx.y;
+  const int c = blockIdx.x;
+  const char* rp = logits + (int64_t)row * row_bytes;
+  const int begin = c * chunk_len;
+  store_slice(block_best(sample_scan<kF32, kVec>(rp, begin, min(V, begin + chunk_len), row, key)), row, c, chunks,
+              tok, part);
+}
 
-__global__ __launch_bounds__(kFuseThreads) void argmax_accept_kernel(
-    int N, int chunks, const float* __restrict__ part_v, const int* __restrict__ part_i, int32_t* tok,
-    const int32_t* __restrict__ parent, const int32_t* __restrict__ draft, int32_t* __restrict__ accept_len,
-    int32_t* __restrict__ accept_nodes, int32_t* __restrict__ accept_tokens, int32_t* __restrict__ bonus,
-    int32_t* dev_error) {
+// One workgroup finishes the verify step: thread i takes node row i's largest slice key
+// (loads batched 16 slices at a time, all unconditional, indices clamped: a repeated key
+// cannot change the maximum), keeps the token in LDS and runs the acceptance walk on the
+// tokens (the walk of tv_accept). The draft and parent entries and the first batch of keys
+// are loaded together, ahead of the tree preprocessing, so that their round trips overlap.
+// With a single slice per row the slice kernel already wrote tok.
+__global__ __launch_bounds__(kBlock) void argmax_accept_kernel(
+    int N, int chunks, const uint64_t* __restrict__ part, int32_t* tok, const int32_t* __restrict__ parent,
+    const int32_t* __restrict__ draft, int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes,
+    int32_t* __restrict__ accept_tokens, int32_t* __restrict__ bonus, int32_t* dev_error) {
+  constexpr int kBatch = 16;
   __shared__ uint64_t anc[kMaxNodes * kAncWords];
   __shared__ int par[kMaxNodes];
   __shared__ int jmp[kMaxNodes];
   __shared__ uint64_t okw[kAncWords];
-  __shared__ uint32_t red[kFuseThreads / 64];
+  __shared__ uint32_t red[kBlock / 64];
   __shared__ int32_t tok_s[kMaxNodes];
   const int i = threadIdx.x;
   const int draft_i = i < N ? draft[i] : 0;
   const int parent_i = i < N ? parent[i] : -1;
   const bool reduce = i < N && chunks > 1;
-  const float* pv = part_v + (int64_t)(reduce ? i : 0) * chunks;
-  const int* pi = part_i + (int64_t)(reduce ? i : 0) * chunks;
-  float v[32];
-  int ix[32];
+  const uint64_t* pk = part + (int64_t)(reduce ? i : 0) * chunks;
+  uint64_t k[kBatch];
   if (reduce) {
 #pragma unroll
-    for (int u = 0; u < 32; ++u) {
-      const int j = min(u, chunks - 1);
-      v[u] = pv[j];
-      ix[u] = pi[j];
-    }
+    for (int u = 0; u < kBatch; ++u) k[u] = pk[min(u, chunks - 1)];
   }
   tree_prep_lds_from(parent_i, N, anc, par, jmp, dev_error);
 
   if (i < N) {
     int32_t t;
     if (chunks > 1) {
-      Best b{-INFINITY, INT_MAX};
-      for (int j0 = 0; j0 < chunks; j0 += 32) {
+      uint64_t best = 0;
+      for (int j0 = 0; j0 < chunks; j0 += kBatch) {
         if (j0 > 0) {
 #pragma unroll
-          for (int u = 0; u < 32; ++u) {
-            const int j = min(j0 + u, chunks - 1);
-            v[u] = pv[j];
-            ix[u] = pi[j];
-          }
+          for (int u = 0; u < kBatch; ++u) k[u] = pk[min(j0 + u, chunks - 1)];
         }
 #pragma unroll
-        for (int u = 0; u < 32; ++u) b = better(b, Best{v[u], ix[u]});
+        for (int u = 0; u < kBatch; ++u) best = k[u] > best ? k[u] : best;
       }
-      t = b.i == INT_MAX ? -1 : b.i;
+      t = key_token(best);
       tok[i] = t;
     } else {
       t = tok[i];
@@ -357,15 +371,16 @@ __global__ __launch_bounds__(kFuseThreads) void argmax_accept_kernel(
     tok_s[i] = t;
   }
   __syncthreads();
-  accept_block<kFuseThreads>(anc, par, tok_s, draft_i, N, okw, red, accept_len, accept_nodes, accept_tokens,
-                             bonus);
+  accept_block<kBlock>(anc, par, tok_s, draft_i, N, okw, red, accept_len, accept_nodes, accept_tokens, bonus);
 }
 
 }  // namespace
 
 ArgmaxPlan argmax_plan(int N, int V, int dtype, bool vec) {
   // One slice = kUnroll 16-byte loads per thread: 8192 bf16 or 4096 fp32 elements. The
-  // scalar path (rows not 16-byte aligned) uses 4096-element slices.
+  // scalar path (rows not 16-byte aligned) uses 4096-element slices. (Eight loads per
+  // thread, with half as many workgroups, measured slower: 7.7 against 6.5 us for
+  // [64, 152064] bf16.)
   (void)N;
   ArgmaxPlan p;
   p.chunk_len = (vec && dtype == TV_BF16) ? kBlock * 8 * kUnroll : kBlock * 4 * kUnroll;
@@ -373,33 +388,30 @@ ArgmaxPlan argmax_plan(int N, int V, int dtype, bool vec) {
   return p;
 }
 
+// Workspace: one 64-bit key per (row, slice), sized for the most slices any path uses.
 size_t argmax_workspace_bytes(int N, int V) {
-  const ArgmaxPlan p = argmax_plan(N, V, TV_F32, false);  // the most slices of any path
-  const size_t parts = (size_t)N * p.chunks;
-  size_t bytes = (parts * sizeof(float) + 255) / 256 * 256;
-  bytes += parts * sizeof(int);
-  return (bytes + 255) / 256 * 256;
+  const ArgmaxPlan p = argmax_plan(N, V, TV_F32, false);
+  return ((size_t)N * p.chunks * sizeof(uint64_t) + 255) / 256 * 256;
 }
 
 hipError_t launch_argmax_partial(const void* logits, int dtype, int N, int V, int64_t row_bytes, bool vec,
-                                 const ArgmaxPlan& p, int32_t* tok, float* part_v, int* part_i,
-                                 hipStream_t stream) {
+                                 const ArgmaxPlan& p, int32_t* tok, uint64_t* part, hipStream_t stream) {
   const dim3 grid(p.chunks, N);
   const char* lg = static_cast<const char*>(logits);
   if (dtype == TV_F32) {
     if (vec)
       hipLaunchKernelGGL((argmax_partial<true, true>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes, p.chunks,
-                         p.chunk_len, tok, part_v, part_i);
+                         p.chunk_len, tok, part);
     else
       hipLaunchKernelGGL((argmax_partial<true, false>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes, p.chunks,
-                         p.chunk_len, tok, part_v, part_i);
+                         p.chunk_len, tok, part);
   } else {
     if (vec)
       hipLaunchKernelGGL((argmax_partial<false, true>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes, p.chunks,
-                         p.chunk_len, tok, part_v, part_i);
+                         p.chunk_len, tok, part);
     else
       hipLaunchKernelGGL((argmax_partial<false, false>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes, p.chunks,
-                         p.chunk_len, tok, part_v, part_i);
+                         p.chunk_len, tok, part);
   }
   return hipGetLastError();
 }
@@ -410,19 +422,12 @@ hipError_t launch_argmax(const void* logits, int dtype, int N, int V, int64_t ro
   const int64_t row_bytes = row_stride * esize;
   const bool vec = ((uintptr_t)logits % 16 == 0) && (row_bytes % 16 == 0);
   const ArgmaxPlan p = argmax_plan(N, V, dtype, vec);
-  const size_t parts = (size_t)N * argmax_plan(N, V, TV_F32, false).chunks;
-  char* ws = static_cast<char*>(workspace);
-  float* part_v = reinterpret_cast<float*>(ws);
-  int* part_i = reinterpret_cast<int*>(ws + (parts * sizeof(float) + 255) / 256 * 256);
-  hipError_t e = launch_argmax_partial(logits, dtype, N, V, row_bytes, vec, p, tok, part_v, part_i, stream);
+  uint64_t* part = static_cast<uint64_t*>(workspace);
+  hipError_t e = launch_argmax_partial(logits, dtype, N, V, row_bytes, vec, p, tok, part, stream);
   if (e != hipSuccess || p.chunks == 1) return e;
-  hipLaunchKernelGGL(argmax_final, dim3((N + 3) / 4), dim3(256), 0, stream, N, p.chunks, part_v, part_i, tok);
+  hipLaunchKernelGGL(argmax_final, dim3((N + 3) / 4), dim3(256), 0, stream, N, p.chunks, part, tok);
   return hipGetLastError();
 }
-
-}  // namespace tv
-
-namespace tv {
 
 hipError_t launch_argmax_accept(const void* logits, int dtype, int N, int V, int64_t row_stride,
                                 const int32_t* parent, const int32_t* draft, int32_t* tok,
@@ -433,20 +438,13 @@ hipError_t launch_argmax_accept(const void* logits, int dtype, int N, int V, int
   const int64_t row_bytes = row_stride * esize;
   const bool vec = ((uintptr_t)logits % 16 == 0) && (row_bytes % 16 == 0);
   const ArgmaxPlan p = argmax_plan(N, V, dtype, vec);
-  const size_t parts = (size_t)N * argmax_plan(N, V, TV_F32, false).chunks;
-  char* ws = static_cast<char*>(workspace);
-  float* part_v = reinterpret_cast<float*>(ws);
-  int* part_i = reinterpret_cast<int*>(ws + (parts * sizeof(float) + 255) / 256 * 256);
-  hipError_t e = launch_argmax_partial(logits, dtype, N, V, row_bytes, vec, p, tok, part_v, part_i, stream);
+  uint64_t* part = static_cast<uint64_t*>(workspace);
+  hipError_t e = launch_argmax_partial(logits, dtype, N, V, row_bytes, vec, p, tok, part, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(argmax_accept_kernel, dim3(1), dim3(kFuseThreads), 0, stream, N, p.chunks, part_v, part_i,
-                     tok, parent, draft, accept_len, accept_nodes, accept_tokens, bonus, dev_error);
+  hipLaunchKernelGGL(argmax_accept_kernel, dim3(1), dim3(kBlock), 0, stream, N, p.chunks, part, tok, parent, draft,
+                     accept_len, accept_nodes, accept_tokens, bonus, dev_error);
   return hipGetLastError();
 }
-
-}  // namespace tv
-
-namespace tv {
 
 hipError_t launch_sample_accept(const void* logits, int dtype, int N, int V, int64_t row_stride, float temperature,
                                 uint64_t seed, uint64_t offset, const int32_t* parent, const int32_t* draft,
@@ -456,10 +454,7 @@ hipError_t launch_sample_accept(const void* logits, int dtype, int N, int V, int
   const int64_t row_bytes = row_stride * esize;
   const bool vec = ((uintptr_t)logits % 16 == 0) && (row_bytes % 16 == 0);
   const ArgmaxPlan p = argmax_plan(N, V, dtype, vec);
-  const size_t parts = (size_t)N * argmax_plan(N, V, TV_F32, false).chunks;
-  char* ws = static_cast<char*>(workspace);
-  float* part_v = reinterpret_cast<float*>(ws);
-  int* part_i = reinterpret_cast<int*>(ws + (parts * sizeof(float) + 255) / 256 * 256);
+  uint64_t* part = static_cast<uint64_t*>(workspace);
   SampleKey key{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)offset, (uint32_t)(offset >> 32),
                 (float)(1.4426950408889634 / (double)temperature)};
   const dim3 grid(p.chunks, N);
@@ -467,22 +462,22 @@ hipError_t launch_sample_accept(const void* logits, int dtype, int N, int V, int
   if (dtype == TV_F32) {
     if (vec)
       hipLaunchKernelGGL((sample_partial<true, true>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes, p.chunks,
-                         p.chunk_len, key, tok, part_v, part_i);
+                         p.chunk_len, key, tok, part);
     else
       hipLaunchKernelGGL((sample_partial<true, false>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes, p.chunks,
-                         p.chunk_len, key, tok, part_v, part_i);
+                         p.chunk_len, key, tok, part);
   } else {
     if (vec)
       hipLaunchKernelGGL((sample_partial<false, true>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes, p.chunks,
-                         p.chunk_len, key, tok, part_v, part_i);
+                         p.chunk_len, key, tok, part);
     else
       hipLaunchKernelGGL((sample_partial<false, false>), grid, dim3(kBlock), 0, stream, lg, V, row_bytes, p.chunks,
-                         p.chunk_len, key, tok, part_v, part_i);
+                         p.chunk_len, key, tok, part);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(argmax_accept_kernel, dim3(1), dim3(kFuseThreads), 0, stream, N, p.chunks, part_v, part_i,
-                     tok, parent, draft, accept_len, accept_nodes, accept_tokens, bonus, dev_error);
+  hipLaunchKernelGGL(argmax_accept_kernel, dim3(1), dim3(kBlock), 0, stream, N, p.chunks, part, tok, parent, draft,
+                     accept_len, accept_nodes, accept_tokens, bonus, dev_error);
   return hipGetLastError();
 }
 
