@@ -45,10 +45,10 @@ CPU_SAMPLE_SECONDS = 10.0
 # profiles/tv_tree_attn_long_128k_hbm_counters.md. Valid only for the kernel sources they
 # were taken on (compared through a digest of their code without comments): reported as
 # null once that code changes.
-TRAFFIC_BYTES_PER_CALL = 572938003
+TRAFFIC_BYTES_PER_CALL = 572969312
 TRAFFIC_SOURCES = ("draft_tree_verification_tv_amd/csrc/tv_attn.hip",
                    "draft_tree_verification_tv_amd/csrc/tv_internal.h")
-TRAFFIC_SOURCES_SHA256 = "f9efc977bcc27b1c9360e59875e52579953917792a866ae444a392bcd7be218f"
+TRAFFIC_SOURCES_SHA256 = "d232c69f99c44e7267bbdfeb390a1e959ecbfd0dd3bd43d5c1e0270096e28035"
 
 
 def code_digest(root, files):
@@ -88,7 +88,9 @@ def measure_ceilings(K, Vc, T, Hkv, D, layers, stream, attn_call):
 
     dev = K.device
     row_b = D * 2
-    nl = min(layers, 8)
+    # the layers' caches after the first (at most 8), or the first alone
+    first = 1 if layers > 1 else 0
+    nl = max(1, min(layers - 1, 8))
     sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
 
     def timed_bytes(launch, nbytes, rounds=3):
@@ -112,7 +114,7 @@ def measure_ceilings(K, Vc, T, Hkv, D, layers, stream, attn_call):
 
         def run_contig(rpw=rpw):
             for buf in (K, Vc):
-                probe.stream_read(buf[1:1 + nl], span_rows, 4096, 4096, 1, rpw, sink)
+                probe.stream_read(buf[first:first + nl], span_rows, 4096, 4096, 1, rpw, sink)
         contiguous[grid] = timed_bytes(run_contig, 2 * span_rows * 4096)
 
     # (b) the KV pattern: column = KV head, rows = keys
@@ -121,7 +123,7 @@ def measure_ceilings(K, Vc, T, Hkv, D, layers, stream, attn_call):
         rpw = -(-T // ranges)
 
         def run_kv(rpw=rpw):
-            for b in range(1, 1 + nl):
+            for b in range(first, first + nl):
                 probe.stream_read(K[b], T, row_b, Hkv * row_b, Hkv, rpw, sink)
                 probe.stream_read(Vc[b], T, row_b, Hkv * row_b, Hkv, rpw, sink)
         pattern[ranges] = timed_bytes(run_kv, 2 * nl * T * Hkv * row_b)
@@ -151,12 +153,12 @@ def measure_ceilings(K, Vc, T, Hkv, D, layers, stream, attn_call):
         return c / t * rt_hz / 1e9
 
     ticks_3ms = int(3e-3 * rt_hz)
-    attn_ghz = clock_under(lambda: [attn_call(1 + b % (layers - 1)) for b in range(4)],
-                           lambda: [attn_call(1 + b % (layers - 1)) for b in range(4, 44)], ticks_3ms)
+    attn_ghz = clock_under(lambda: [attn_call(first + b % nl) for b in range(4)],
+                           lambda: [attn_call(first + b % nl) for b in range(4, 44)], ticks_3ms)
 
     def kv_reads(n):
         for i in range(n):
-            b = 1 + i % nl
+            b = first + i % nl
             probe.stream_read(K[b], T, row_b, Hkv * row_b, Hkv, -(-T // 64), sink)
             probe.stream_read(Vc[b], T, row_b, Hkv * row_b, Hkv, -(-T // 64), sink)
     read_ghz = clock_under(lambda: kv_reads(2), lambda: kv_reads(30), ticks_3ms)

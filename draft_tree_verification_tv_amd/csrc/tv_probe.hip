@@ -1,8 +1,9 @@
 // Measurement probes for the benchmark (libtv_probe.so; declarations in include/tv_probe.h).
 // They compute nothing of the verify step: one streams bytes from HBM so that the
 // attention kernel's bandwidth can be set against what a plain read achieves on the same
-// chip and access pattern; the other counts shader clocks against the constant-rate
-// real-time counter to give the clock the chip actually runs at under a given load.
+// chip and access pattern; one counts shader clocks against the constant-rate real-time
+// counter to give the clock the chip actually runs at under a given load; one times MFMA
+// and VALU instruction mixes in shader cycles (how far a wave overlaps the two).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -67,6 +68,68 @@ __global__ __launch_bounds__(64) void clock_kernel(uint64_t* __restrict__ out, u
   }
 }
 
+// One workgroup: `iters` iterations of eight 32x32x16 bf16 MFMAs (four independent
+// accumulators) and/or VALU work, in the instruction mix `MODE` names; each wave stores
+// its shader-clock cycle count. Modes: 0 MFMA only; 1 64 fp32 FMAs per iteration (eight
+// independent chains); 2 MFMA each followed by 8 FMAs; 3 MFMA each followed by 4 exp2 and
+// 4 FMAs; 4 64 exp2 per iteration; 5 MFMA each followed by 2 exp2 and 6 FMAs. The
+// interleaved modes are kept in that order by scheduling-group barriers.
+template <int MODE>
+__global__ __launch_bounds__(512) void coissue_kernel(const float* __restrict__ in, float* __restrict__ out,
+                                                      uint64_t* __restrict__ cyc, int iters) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(in[lane] * i);
+    b[i] = (__bf16)(in[lane + 1] * i);
+  }
+  f32x16 acc[4];
+  for (int k = 0; k < 4; ++k) acc[k] = f32x16{};
+  float x[8];
+  for (int j = 0; j < 8; ++j) x[j] = in[j + lane];
+  const float c0 = in[100], c1 = in[101];
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      if (MODE != 1 && MODE != 4) acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[m & 3], 0, 0, 0);
+      if (MODE == 1 || MODE == 2) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = __builtin_fmaf(x[j], c0, c1);
+      }
+      if (MODE == 3) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = __builtin_amdgcn_exp2f(x[j]);
+#pragma unroll
+        for (int j = 4; j < 8; ++j) x[j] = __builtin_fmaf(x[j], c0, c1);
+      }
+      if (MODE == 4) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = __builtin_amdgcn_exp2f(x[j]);
+      }
+      if (MODE == 5) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) x[j] = __builtin_amdgcn_exp2f(x[j]);
+#pragma unroll
+        for (int j = 2; j < 8; ++j) x[j] = __builtin_fmaf(x[j], c0, c1);
+      }
+      if (MODE == 2 || MODE == 3 || MODE == 5) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      }
+    }
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  float sum = 0.f;
+  for (int k = 0; k < 4; ++k)
+    for (int e = 0; e < 16; ++e) sum += acc[k][e];
+  for (int j = 0; j < 8; ++j) sum += x[j];
+  out[threadIdx.x] = sum;
+  if (lane == 0) cyc[threadIdx.x >> 6] = t1 - t0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -85,6 +148,22 @@ int tv_probe_stream_read(const void* base, int64_t rows, int row_bytes, int64_t 
   hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)(groups * cols)), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const char*>(base), rows, shift, row_stride,
                      cols, rows_per_wg, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+int tv_probe_coissue(int mode, int threads, int iters, const float* in, float* out, uint64_t* cycles,
+                     void* stream) {
+  if (!in || !out || !cycles || iters < 1 || (threads != 64 && threads != 256 && threads != 512)) return 1;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(coissue_kernel<0>, dim3(1), dim3(threads), 0, st, in, out, cycles, iters); break;
+    case 1: hipLaunchKernelGGL(coissue_kernel<1>, dim3(1), dim3(threads), 0, st, in, out, cycles, iters); break;
+    case 2: hipLaunchKernelGGL(coissue_kernel<2>, dim3(1), dim3(threads), 0, st, in, out, cycles, iters); break;
+    case 3: hipLaunchKernelGGL(coissue_kernel<3>, dim3(1), dim3(threads), 0, st, in, out, cycles, iters); break;
+    case 4: hipLaunchKernelGGL(coissue_kernel<4>, dim3(1), dim3(threads), 0, st, in, out, cycles, iters); break;
+    case 5: hipLaunchKernelGGL(coissue_kernel<5>, dim3(1), dim3(threads), 0, st, in, out, cycles, iters); break;
+    default: return 1;
+  }
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 

@@ -18,7 +18,10 @@ from .build import PROBE_LIB_PATH
 _lib = None
 _lock = threading.Lock()
 
-EXPORTS = ("tv_probe_stream_read", "tv_probe_clock")
+EXPORTS = ("tv_probe_stream_read", "tv_probe_clock", "tv_probe_coissue")
+
+COISSUE_MODES = ("MFMA only (8 per iteration)", "VALU only (64 FMA)", "MFMA + 8 FMA each",
+                 "MFMA + 4 exp2 + 4 FMA each", "exp2 only (64)", "MFMA + 2 exp2 + 6 FMA each")
 
 
 def lib():
@@ -36,6 +39,8 @@ def lib():
             L.tv_probe_stream_read.argtypes = [vp, i64, i32, i64, i32, i64, vp, vp]
             L.tv_probe_clock.restype = i32
             L.tv_probe_clock.argtypes = [vp, ctypes.c_uint64, vp]
+            L.tv_probe_coissue.restype = i32
+            L.tv_probe_coissue.argtypes = [i32, i32, i32, vp, vp, vp, vp]
             _lib = L
     return _lib
 
@@ -74,3 +79,34 @@ def clock(out: torch.Tensor, ticks: int, stream=None):
     st = lib().tv_probe_clock(out.data_ptr(), int(ticks), _stream(stream))
     if st != 0:
         raise RuntimeError(f"tv_probe_clock failed with status {st}")
+
+
+def coissue(mode: int, threads: int, iters: int = 2000):
+    """Shader-clock cycles per iteration of instruction mix ``mode`` (COISSUE_MODES), the
+    mean over the workgroup's waves (one workgroup of ``threads`` threads, so 64 gives one
+    wave alone on a SIMD and 512 two waves on every SIMD of a CU)."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    src = (torch.arange(1024, device=dev, dtype=torch.float32) % 17) * 1e-3
+    out = torch.empty(512, dtype=torch.float32, device=dev)
+    cyc = torch.zeros(8, dtype=torch.int64, device=dev)
+    for _ in range(2):  # the first launch loads the code
+        st = lib().tv_probe_coissue(int(mode), int(threads), int(iters), src.data_ptr(), out.data_ptr(),
+                                    cyc.data_ptr(), _stream(None))
+        if st != 0:
+            raise RuntimeError(f"tv_probe_coissue failed with status {st}")
+        torch.cuda.synchronize()
+    waves = threads // 64
+    return float(cyc[:waves].double().mean()) / iters
+
+
+def main():
+    """Print the MFMA/VALU co-issue table: python -m draft_tree_verification_tv_amd.probe"""
+    torch.cuda.init()
+    for threads in (64, 512):
+        for mode, name in enumerate(COISSUE_MODES):
+            c = coissue(mode, threads)
+            print(f"{name:30s} waves/workgroup={threads // 64}  cycles/iteration={c:7.1f}", flush=True)
+
+
+if __name__ == "__main__":
+    main()

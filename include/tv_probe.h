@@ -1,13 +1,15 @@
 /*
  * tv_probe.h -- measurement probes that the benchmark runs beside libtv (libtv_probe.so).
  *
- * Neither probe is part of the verify step. They give the two ceilings that the attention
+ * None of the probes is part of the verify step. Two give the ceilings that the attention
  * kernel's bandwidth is set against on the machine it runs on:
  *   - the rate at which plain reads stream from HBM, contiguous or in the KV cache's
  *     pattern (one KV head's 256-byte rows every Hkv * 256 bytes);
  *   - the shader clock the chip runs at under a given load (it drops below the nominal
  *     2.4 GHz when power limits bind).
- * Pointers are device pointers; `stream` is a hipStream_t passed as void*. Both calls
+ * The third times MFMA and VALU instruction mixes in shader cycles: how far one wave, or
+ * two sharing a SIMD, overlap matrix and vector work.
+ * Pointers are device pointers; `stream` is a hipStream_t passed as void*. The calls
  * only enqueue work. They return 0 on success, 1 for an invalid argument and 5 when the
  * HIP runtime refuses the launch.
  */
@@ -38,6 +40,19 @@ int tv_probe_stream_read(const void* base, int64_t rows, int row_bytes, int64_t 
  * ratio times the real-time rate is the shader clock over the spin. 1 <= ticks <= 1e8.
  */
 int tv_probe_clock(uint64_t* out, uint64_t ticks, void* stream);
+
+/*
+ * One workgroup of `threads` (64, 256 or 512) threads runs `iters` iterations of an
+ * instruction mix and each wave writes its shader-clock cycle count to cycles[wave]
+ * (uint64 [threads / 64]). Every iteration issues eight v_mfma_f32_32x32x16_bf16 on four
+ * independent accumulators and/or VALU work: mode 0 MFMAs only; 1 64 fp32 FMAs (eight
+ * independent chains); 2 each MFMA followed by 8 FMAs; 3 each MFMA followed by 4 exp2 and
+ * 4 FMAs; 4 64 exp2; 5 each MFMA followed by 2 exp2 and 6 FMAs. `in` (fp32, >= 128
+ * values) seeds the operands; `out` (fp32 [threads]) receives a checksum so that no work
+ * is dead. Returns 1 for an invalid argument.
+ */
+int tv_probe_coissue(int mode, int threads, int iters, const float* in, float* out, uint64_t* cycles,
+                     void* stream);
 
 #ifdef __cplusplus
 }

@@ -276,6 +276,10 @@ def test_probe_library_exports_and_validation():
     assert L.tv_probe_stream_read(FAKE, 0, 256, 2048, 8, 4, sink, None) == 1           # no rows
     assert L.tv_probe_clock(None, 100, None) == 1
     assert L.tv_probe_clock(FAKE, 0, None) == 1
+    assert L.tv_probe_coissue(0, 64, 10, None, FAKE, FAKE, None) == 1    # null input
+    assert L.tv_probe_coissue(0, 100, 10, FAKE, FAKE, FAKE, None) == 1   # not 64, 256 or 512 threads
+    assert L.tv_probe_coissue(0, 64, 0, FAKE, FAKE, FAKE, None) == 1     # no iterations
+    assert L.tv_probe_coissue(6, 64, 10, FAKE, FAKE, FAKE, None) == 1    # no such mode
 
 
 def noalloc_call(**kw):
