@@ -45,10 +45,10 @@ CPU_SAMPLE_SECONDS = 10.0
 # profiles/tv_tree_attn_long_128k_hbm_counters.md. Valid only for the kernel sources they
 # were taken on (compared through a digest of their code without comments): reported as
 # null once that code changes.
-TRAFFIC_BYTES_PER_CALL = 572969312
+TRAFFIC_BYTES_PER_CALL = 572942354
 TRAFFIC_SOURCES = ("draft_tree_verification_tv_amd/csrc/tv_attn.hip",
                    "draft_tree_verification_tv_amd/csrc/tv_internal.h")
-TRAFFIC_SOURCES_SHA256 = "d232c69f99c44e7267bbdfeb390a1e959ecbfd0dd3bd43d5c1e0270096e28035"
+TRAFFIC_SOURCES_SHA256 = "bd4c964dfa6925933a7697a5e6636edbd6e7bc4751c9decdbe2485104f460f95"
 
 
 def code_digest(root, files):

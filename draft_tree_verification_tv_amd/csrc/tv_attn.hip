@@ -36,7 +36,9 @@
 //   * Software pipeline. Every wave walks its keys in 32-key blocks. While it turns block j
 //     into probabilities it already issues the score MFMAs of block j+1 (into the other of
 //     two score buffers), then block j's P.V MFMAs: MFMA and VALU work of one wave overlap,
-//     and the two waves sharing a SIMD fill each other's stalls.
+//     and the two waves sharing a SIMD fill each other's stalls. In the 256-row kernel the
+//     K fragments of block j+2 are read before block j's P.V, so score MFMAs find their
+//     operands in registers.
 //   * Softmax. exp2 with the scale folded into one FMA, against a lazy reference maximum
 //     that moves only when a block would exceed it by more than 2^8; whether it must is
 //     read off the probabilities themselves (a lane's sum of 16 above 2^8), so the block
@@ -413,10 +415,21 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
     } else {
       win = (uint32_t)((a[0] << (-d)) | ((1ull << (-d)) - 1ull));
     }
+    // Element e holds key 8 * (e / 4) + 4 * grp + e % 4 of the block. The bf16 kernels
+    // shift the window by 4 * grp once, leaving a constant bit per element (16 fewer live
+    // registers); the FP8 kernels keep the per-element shift, measured faster there.
+    if constexpr (kF8) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int b = 8 * (e >> 2) + 4 * grp + (e & 3);  // key within the block
-      if (!((win >> b) & 1u)) sc[c][e] = -INFINITY;
+      for (int e = 0; e < 16; ++e) {
+        const int b = 8 * (e >> 2) + 4 * grp + (e & 3);
+        if (!((win >> b) & 1u)) sc[c][e] = -INFINITY;
+      }
+    } else {
+      const uint32_t wl = win >> (4 * grp);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if (!(wl & (1u << (8 * (e >> 2) + (e & 3))))) sc[c][e] = -INFINITY;
+      }
     }
   };
 
@@ -838,36 +851,67 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
     barrier_keep<DPT>();
   else
     barrier_keep<0>();
+  // The K fragments of the next block to score are read from LDS one sub-step ahead, into
+  // kf, right after this block's softmax and before its P.V product, so the score MFMAs of
+  // a sub-step never wait for LDS. Within step t the block after the successor lies in
+  // tile t or t+1, both landed by the barrier that closed step t-1 (step 0 waits for tile
+  // 1 midway, before its first read of it).
+  bf16x8 kf[8];
+  auto kload = [&](const char* Kt, int kb) __attribute__((always_inline)) {
+    const char* Ks = Kt + kb * 32 * ROWB;
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) kf[s8] = *reinterpret_cast<const bf16x8*>(Ks + koff[s8]);
+  };
+  // Sub-step over block (t, kb) with successor (tn, kb ^ 1), whose fragments are in kf: the
+  // successor's score MFMAs beside this block's softmax (one scheduling region), then the
+  // reads of the block after the successor (block kbnn of the K tile at Knn, if nn), this
+  // block's P.V MFMAs, and the successor's mask.
+  auto sub_kf = [&](int t, auto kbc, int tn, const char* Knn, int kbnn, bool nn, const char* Vt)
+                    __attribute__((always_inline)) {
+    constexpr int kb = decltype(kbc)::value;
+    constexpr int kbn = kb ^ 1;
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) acc = mfma32(kf[s8], qf[s8], acc);
+    sc[kbn] = acc;
+    softmax(kb);
+    __builtin_amdgcn_sched_barrier(0);
+    if (nn) kload(Knn, kbnn);
+    pv(Vt, kb);
+    if (tn >= nplain) mask(kbeg + tn * KT + kbn * 32, kbn);
+  };
   qk(kstage(0), 0, 0);
   if (nplain == 0) mask(kbeg, 0);
+  kload(kstage(0), 1);
 
-  // Tile t: block 0 (successor: block 1 of tile t), block 1 (successor: block 0 of tile
-  // t+1); the barrier after each tile guarantees tile t+2 and keeps tile t+3 in flight.
-  // Stage reuse: tile t+3 overwrites tile t-1, whose last reads were in tile t-1's blocks.
-  // Unrolled by the ring length so that stage offsets are constants (folded into the
-  // ds_read offsets); the up to three steps left over use computed stages.
+  // Tile t: block 0 (successor: block 1 of tile t; reads block 0 of tile t+1), block 1
+  // (successor: block 0 of tile t+1; reads block 1 of tile t+1); the barrier after each
+  // tile guarantees tile t+2 and keeps tile t+3 in flight. Stage reuse: tile t+3
+  // overwrites tile t-1, whose last reads were in tile t-1's blocks. Unrolled by the ring
+  // length so that stage offsets are constants (folded into the ds_read offsets); the up
+  // to three steps left over use computed stages.
   auto step = [&](int t, auto stc) __attribute__((always_inline)) {
     constexpr int st = decltype(stc)::value;
     if (t + 3 < ntiles) issue(t + 3);
-    const char* K0 = smem + st * TILE_B;
     const char* K1 = smem + ((st + 1) & (NSTAGE - 1)) * TILE_B;
     const char* V0 = smem + st * TILE_B;
-    sub(t, B0{}, t, K0, V0);
-    sub(t, B1{}, t + 1, K1, V0);
+    sub_kf(t, B0{}, t, K1, 0, true, V0);
+    sub_kf(t, B1{}, t + 1, K1, 1, true, V0);
     wait_step(t);
   };
   int t = 0;
   if (ntiles > 1) {
-    // Step 0: tile 1 must land before block 1's successor (block 0 of tile 1) is scored.
+    // Step 0: tile 1 must land before the block after block 0's successor is read.
     if (3 < ntiles) issue(3);
-    sub(0, B0{}, 0, kstage(0), vstage(0));
+    sub_kf(0, B0{}, 0, nullptr, 0, false, vstage(0));
     if (ntiles > 3)
       barrier_keep<2 * DPT>();
     else if (ntiles > 2)
       barrier_keep<DPT>();
     else
       barrier_keep<0>();
-    sub(0, B1{}, 1, kstage(1), vstage(0));
+    kload(kstage(1), 0);
+    sub_kf(0, B1{}, 1, kstage(1), 1, true, vstage(0));
     wait_step(0);
     t = 1;
   }
@@ -879,13 +923,13 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
   }
   for (; t + 1 < ntiles; ++t) {
     if (t + 3 < ntiles) issue(t + 3);
-    sub(t, B0{}, t, kstage(t), vstage(t));
-    sub(t, B1{}, t + 1, kstage(t + 1), vstage(t));
+    sub_kf(t, B0{}, t, kstage(t + 1), 0, true, vstage(t));
+    sub_kf(t, B1{}, t + 1, kstage(t + 1), 1, true, vstage(t));
     wait_step(t);
   }
   {
     const int t = ntiles - 1;
-    sub(t, B0{}, t, kstage(t), vstage(t));
+    sub_kf(t, B0{}, t, nullptr, 0, false, vstage(t));
     softmax(1);
     pv(vstage(t), 1);
   }

@@ -3,7 +3,9 @@
 // attention kernel's bandwidth can be set against what a plain read achieves on the same
 // chip and access pattern; one counts shader clocks against the constant-rate real-time
 // counter to give the clock the chip actually runs at under a given load; one times MFMA
-// and VALU instruction mixes in shader cycles (how far a wave overlaps the two).
+// and VALU instruction mixes in shader cycles (how far a wave overlaps the two); one runs
+// MFMA streams with LDS reads and VALU work beside them on every CU at once, the mix of
+// the attention loop without its dependencies, for the throughput such a mix can reach.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -130,6 +132,63 @@ __global__ __launch_bounds__(512) void coissue_kernel(const float* __restrict__ 
   if (lane == 0) cyc[threadIdx.x >> 6] = t1 - t0;
 }
 
+// Every CU at once: `iters` iterations of eight v_mfma_f32_32x32x16_bf16 on four
+// independent accumulators. LSTEP 1: each MFMA's A operand is a fresh 16-byte LDS read per
+// lane (1 KB per wave); LSTEP 2: every second one is (0.5 KB per MFMA); 0: none. VALU: each
+// MFMA is followed by one exp2 and four FMAs on independent values. Nothing depends on
+// anything else, so this is the most such a mix can reach. Wave 0 of workgroup 0 records
+// shader cycles and real-time ticks around its loop in clk[0], clk[1].
+template <int LSTEP, bool VALU>
+__global__ __launch_bounds__(512) void mix_kernel(const float* __restrict__ in, float* __restrict__ out,
+                                                  uint64_t* __restrict__ clk, int iters) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  __shared__ __align__(16) char lds[65536];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < 65536 / 4; i += blockDim.x) reinterpret_cast<float*>(lds)[i] = in[i & 1023];
+  __syncthreads();
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(in[lane] * i);
+    b[i] = (__bf16)(in[lane + 1] * i);
+  }
+  float x[4];
+  for (int j = 0; j < 4; ++j) x[j] = in[j + lane] * 1e-3f;
+  const float c0 = in[100], c1 = in[101];
+  uint64_t r0 = 0, t0 = 0;
+  if (blockIdx.x == 0 && tid == 0) {
+    r0 = __builtin_amdgcn_s_memrealtime();
+    t0 = __builtin_amdgcn_s_memtime();
+  }
+  f32x16 acc[4];
+  for (int j = 0; j < 4; ++j) acc[j] = f32x16{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      bf16x8 aa = a;
+      if (LSTEP > 0 && m % LSTEP == 0) {
+        const int off = ((it * 8 + m) * 1024 + lane * 16 + wave * 64) & (65536 - 16);
+        aa = *reinterpret_cast<const bf16x8*>(lds + off);
+      }
+      acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa, b, acc[m & 3], 0, 0, 0);
+      if (VALU) {
+        x[0] = __builtin_amdgcn_exp2f(x[0] * 1e-3f);
+#pragma unroll
+        for (int j = 1; j < 4; ++j) x[j] = __builtin_fmaf(x[j], c0, c1);
+      }
+    }
+  }
+  float sum = 0.f;
+  for (int j = 0; j < 4; ++j)
+    for (int e = 0; e < 16; ++e) sum += acc[j][e];
+  for (int j = 0; j < 4; ++j) sum += x[j];
+  out[(int64_t)blockIdx.x * blockDim.x + tid] = sum;
+  if (blockIdx.x == 0 && tid == 0) {
+    clk[0] = __builtin_amdgcn_s_memtime() - t0;
+    clk[1] = __builtin_amdgcn_s_memrealtime() - r0;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -170,6 +229,25 @@ int tv_probe_coissue(int mode, int threads, int iters, const float* in, float* o
 int tv_probe_clock(uint64_t* out, uint64_t ticks, void* stream) {
   if (!out || ticks < 1 || ticks > 100000000ull) return 1;
   hipLaunchKernelGGL(clock_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), out, ticks);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+int tv_probe_mix(int lds_step, int valu, int threads, int workgroups, int iters, const float* in, float* out,
+                 uint64_t* clk, void* stream) {
+  if (!in || !out || !clk || iters < 1 || workgroups < 1 || workgroups > 65536 || (threads != 256 && threads != 512) ||
+      lds_step < 0 || lds_step > 2 || (valu != 0 && valu != 1))
+    return 1;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 g(workgroups), b(threads);
+  if (valu) {
+    if (lds_step == 0) hipLaunchKernelGGL((mix_kernel<0, true>), g, b, 0, st, in, out, clk, iters);
+    if (lds_step == 1) hipLaunchKernelGGL((mix_kernel<1, true>), g, b, 0, st, in, out, clk, iters);
+    if (lds_step == 2) hipLaunchKernelGGL((mix_kernel<2, true>), g, b, 0, st, in, out, clk, iters);
+  } else {
+    if (lds_step == 0) hipLaunchKernelGGL((mix_kernel<0, false>), g, b, 0, st, in, out, clk, iters);
+    if (lds_step == 1) hipLaunchKernelGGL((mix_kernel<1, false>), g, b, 0, st, in, out, clk, iters);
+    if (lds_step == 2) hipLaunchKernelGGL((mix_kernel<2, false>), g, b, 0, st, in, out, clk, iters);
+  }
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 

@@ -2,7 +2,9 @@
 
 Not part of the verify step: a plain HBM read stream (contiguous or in the KV cache's
 pattern) and a shader-clock counter, the two ceilings the attention kernel's bandwidth is
-set against. Argument marshalling only; raises if the library is missing.
+set against; an MFMA/VALU co-issue timer on one CU; and a whole-chip run of MFMA streams
+with LDS reads and VALU work beside them. Argument marshalling only; raises if the library
+is missing.
 """
 
 from __future__ import annotations
@@ -18,7 +20,7 @@ from .build import PROBE_LIB_PATH
 _lib = None
 _lock = threading.Lock()
 
-EXPORTS = ("tv_probe_stream_read", "tv_probe_clock", "tv_probe_coissue")
+EXPORTS = ("tv_probe_stream_read", "tv_probe_clock", "tv_probe_coissue", "tv_probe_mix")
 
 COISSUE_MODES = ("MFMA only (8 per iteration)", "VALU only (64 FMA)", "MFMA + 8 FMA each",
                  "MFMA + 4 exp2 + 4 FMA each", "exp2 only (64)", "MFMA + 2 exp2 + 6 FMA each")
@@ -41,6 +43,8 @@ def lib():
             L.tv_probe_clock.argtypes = [vp, ctypes.c_uint64, vp]
             L.tv_probe_coissue.restype = i32
             L.tv_probe_coissue.argtypes = [i32, i32, i32, vp, vp, vp, vp]
+            L.tv_probe_mix.restype = i32
+            L.tv_probe_mix.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp]
             _lib = L
     return _lib
 
@@ -99,13 +103,48 @@ def coissue(mode: int, threads: int, iters: int = 2000):
     return float(cyc[:waves].double().mean()) / iters
 
 
+MIX_CASES = ((0, 0, "MFMA only"), (1, 0, "MFMA + 1 KB LDS reads each"), (0, 1, "MFMA + exp2 + 4 FMA each"),
+             (1, 1, "MFMA + 1 KB LDS + exp2 + 4 FMA each"), (2, 1, "MFMA + 0.5 KB LDS + exp2 + 4 FMA each"))
+
+
+def mix(lds_step: int, valu: int, threads: int, iters: int = 20000):
+    """Whole-chip bf16 MFMA throughput (TFLOP/s, from HIP events) and the shader clock (GHz)
+    of the instruction mix (lds_step, valu) with threads / 128 waves per SIMD, one
+    workgroup per CU."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    src = (torch.arange(1024, device=dev, dtype=torch.float32) % 17) * 1e-3
+    out = torch.empty(cus * threads, dtype=torch.float32, device=dev)
+    clk = torch.zeros(2, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(2):  # the first launch loads the code and lets the clock settle
+        e0.record(stream)
+        st = lib().tv_probe_mix(int(lds_step), int(valu), int(threads), cus, int(iters), src.data_ptr(),
+                                out.data_ptr(), clk.data_ptr(), stream.cuda_stream)
+        e1.record(stream)
+        if st != 0:
+            raise RuntimeError(f"tv_probe_mix failed with status {st}")
+        torch.cuda.synchronize()
+        best = e0.elapsed_time(e1) * 1e-3
+    cyc, ticks = (int(v) for v in clk.cpu())
+    flops = 2.0 * 32 * 32 * 16 * 8 * iters * cus * (threads // 64)
+    return flops / best / 1e12, cyc / ticks * 0.1  # the real-time counter runs at 100 MHz
+
+
 def main():
-    """Print the MFMA/VALU co-issue table: python -m draft_tree_verification_tv_amd.probe"""
+    """Print the co-issue and mix tables: python -m draft_tree_verification_tv_amd.probe"""
     torch.cuda.init()
     for threads in (64, 512):
         for mode, name in enumerate(COISSUE_MODES):
             c = coissue(mode, threads)
             print(f"{name:30s} waves/workgroup={threads // 64}  cycles/iteration={c:7.1f}", flush=True)
+    for threads in (512, 256):
+        for lds_step, valu, name in MIX_CASES:
+            tf, ghz = mix(lds_step, valu, threads)
+            print(f"every CU, {threads // 256} wave(s)/SIMD: {name:40s} {tf:7.1f} TFLOP/s  clock {ghz:.3f} GHz",
+                  flush=True)
 
 
 if __name__ == "__main__":

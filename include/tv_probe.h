@@ -8,7 +8,9 @@
  *   - the shader clock the chip runs at under a given load (it drops below the nominal
  *     2.4 GHz when power limits bind).
  * The third times MFMA and VALU instruction mixes in shader cycles: how far one wave, or
- * two sharing a SIMD, overlap matrix and vector work.
+ * two sharing a SIMD, overlap matrix and vector work. The fourth runs MFMA streams with
+ * LDS reads and VALU work beside them on every CU at once: the throughput that the
+ * attention loop's instruction mix can reach with no dependencies between its parts.
  * Pointers are device pointers; `stream` is a hipStream_t passed as void*. The calls
  * only enqueue work. They return 0 on success, 1 for an invalid argument and 5 when the
  * HIP runtime refuses the launch.
@@ -53,6 +55,19 @@ int tv_probe_clock(uint64_t* out, uint64_t ticks, void* stream);
  */
 int tv_probe_coissue(int mode, int threads, int iters, const float* in, float* out, uint64_t* cycles,
                      void* stream);
+
+/*
+ * `workgroups` workgroups of `threads` (256 or 512: one or two waves per SIMD) threads
+ * each run `iters` iterations of eight v_mfma_f32_32x32x16_bf16 on four independent
+ * accumulators. lds_step 1: every MFMA's A operand is a fresh 16-byte-per-lane LDS read
+ * (1 KB per wave and MFMA); 2: every second MFMA's (0.5 KB); 0: no LDS reads. valu 1: each
+ * MFMA is followed by one exp2 and four FMAs on independent values; 0: none. Workgroup 0's
+ * first wave writes clk[0] = shader-clock cycles and clk[1] = real-time ticks around its
+ * loop (uint64 [2]). `in` (fp32, >= 1024 values) seeds the operands; `out` (fp32
+ * [workgroups * threads]) receives a checksum per thread. 1 <= workgroups <= 65536.
+ */
+int tv_probe_mix(int lds_step, int valu, int threads, int workgroups, int iters, const float* in, float* out,
+                 uint64_t* clk, void* stream);
 
 #ifdef __cplusplus
 }
