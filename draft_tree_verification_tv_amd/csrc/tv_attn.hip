@@ -1014,6 +1014,12 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
 // The query, and for the split that reaches the tree the parent entries, are loaded
 // together with the first key block, so their round trips overlap.
 //
+// FP8 cache (kF8): K and V codes and their row exponents come into registers one block
+// ahead; K is widened there (code * 2^e, the key's exponent) into the A fragments, V is
+// widened and written to one private 8 KB stage per wave in the transposed-read layout
+// (the wave's own LDS accesses stay in order, so the previous block's reads precede the
+// writes), then the block proceeds as for bf16.
+//
 // Layouts. Scores S^T = K Q^T per 16-key half: lane l holds keys 4(l/16) + i (i < 4) of
 // query row l % 16, so a row's 32 keys sit in four lanes (l, l^16, l^32, l^48). The P.V
 // product O^T += V^T P^T takes each lane's own eight probabilities as its B fragment, the
@@ -1035,6 +1041,7 @@ constexpr int R16_TREE_OFF = 8 * R16_STAGES * R16_VB;
 constexpr int R16_SMEM_BYTES = R16_TREE_OFF + TREE_BYTES;
 static_assert(R16_SMEM_BYTES <= 160 * 1024, "16-row kernel LDS");
 
+template <bool kF8>
 __global__ __launch_bounds__(512) void attn_rows16_kernel(SplitParams p) {
   constexpr int NW = 8;
   extern __shared__ __align__(16) char smem[];
@@ -1078,9 +1085,10 @@ __global__ __launch_bounds__(512) void attn_rows16_kernel(SplitParams p) {
     }
   }
 
-  const char* kb8 = static_cast<const char*>(p.k) + (int64_t)h * p.sh * 2;
-  const char* vb8 = static_cast<const char*>(p.v) + (int64_t)h * p.sh * 2;
-  const uint32_t rowstride_b = (uint32_t)p.st * 2u;
+  constexpr int ESZ = kF8 ? 1 : 2;  // bytes per cache element
+  const char* kb8 = static_cast<const char*>(p.k) + (int64_t)h * p.sh * ESZ;
+  const char* vb8 = static_cast<const char*>(p.v) + (int64_t)h * p.sh * ESZ;
+  const uint32_t rowstride_b = (uint32_t)p.st * (uint32_t)ESZ;
   const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
   const uint32_t vpriv = lds_base + (uint32_t)(wave * R16_STAGES * R16_VB);
   const char* vprivp = smem + wave * R16_STAGES * R16_VB;
@@ -1199,28 +1207,113 @@ __global__ __launch_bounds__(512) void attn_rows16_kernel(SplitParams p) {
     }
   };
 
-  bf16x8 kf0[8], kf1[8];
-  int b = wave;
-  if (b < nblk) load_block(b, kf0, 0);
-  if (tree) tree_prep_lds_from(parent_i, p.N, anc, par, jmp, p.dev_error);
-  // Block b + 8's 16 operations are issued before block b's are awaited: vmcnt(16) leaves
-  // exactly them in flight (older loads, the query's included, have landed by then).
-  for (; b < nblk; b += 16) {
-    if (b + 8 < nblk) {
-      load_block(b + 8, kf1, 1);
-      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (!kF8) {
+    bf16x8 kf0[8], kf1[8];
+    int b = wave;
+    if (b < nblk) load_block(b, kf0, 0);
+    if (tree) tree_prep_lds_from(parent_i, p.N, anc, par, jmp, p.dev_error);
+    // Block b + 8's 16 operations are issued before block b's are awaited: vmcnt(16)
+    // leaves exactly them in flight (older loads, the query's included, have landed).
+    for (; b < nblk; b += 16) {
+      if (b + 8 < nblk) {
+        load_block(b + 8, kf1, 1);
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      compute_block(b, kf0, 0);
+      if (b + 8 >= nblk) break;
+      if (b + 16 < nblk) {
+        load_block(b + 16, kf0, 0);
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      compute_block(b + 8, kf1, 1);
     }
-    compute_block(b, kf0, 0);
-    if (b + 8 >= nblk) break;
-    if (b + 16 < nblk) {
-      load_block(b + 16, kf0, 0);
-      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    // Codes and exponents of one 32-key block in registers: K for keys 16 hh + i16, dims
+    // 32 c + 8 g .. + 7 (8 codes each); V for key row vr = lane / 2, dims 64 vh .. + 63.
+    // All loads go to registers, so the compiler's own waits order them.
+    const int32_t* ekp = uniform_ptr(p.ek);
+    const int32_t* evp = uniform_ptr(p.ev);
+    const int vr = lane >> 1, vh = lane & 1;
+    bool bad_exp = false;
+    auto scale_of = [&](int e) __attribute__((always_inline)) -> float {
+      bad_exp |= e < kExpMin || e > kExpMax;
+      e = min(max(e, kExpMin), kExpMax);
+      return __int_as_float((e + 127) << 23);
+    };
+    struct Raw {
+      uint2 k[8];
+      int ek[2];
+      u32x4 v[4];
+      int ev;
+    };
+    auto load_raw = [&](int b, Raw& r) __attribute__((always_inline)) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int key = min(kbeg + b * 32 + 16 * hh + i16, p.T - 1);
+        const char* row = kb8 + (uint32_t)key * rowstride_b + g * 8;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) r.k[4 * hh + c] = *reinterpret_cast<const uint2*>(row + c * 32);
+        r.ek[hh] = ekp[(int64_t)key * p.Hkv + h];
+      }
+      const int kv = min(kbeg + b * 32 + vr, p.T - 1);
+      const char* vrow = vb8 + (uint32_t)kv * rowstride_b + vh * 64;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r.v[j] = *reinterpret_cast<const u32x4*>(vrow + j * 16);
+      r.ev = evp[(int64_t)kv * p.Hkv + h];
+    };
+    auto compute_raw = [&](int b, const Raw& r) __attribute__((always_inline)) {
+      // V: widen 64 codes of row vr and write them as logical chunks 8 vh .. 8 vh + 7
+      char* vst = smem + wave * R16_STAGES * R16_VB;
+      const float svv = scale_of(r.ev);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4 lo, hi;
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          lo[2 * q2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.v[j][q2], svv, false));
+          lo[2 * q2 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.v[j][q2], svv, true));
+          hi[2 * q2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.v[j][q2 + 2], svv, false));
+          hi[2 * q2 + 1] =
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.v[j][q2 + 2], svv, true));
+        }
+        const int c = vh * 8 + 2 * j;
+        *reinterpret_cast<u32x4*>(vst + vr * ROWB + ((c ^ swz_v16(vr)) << 4)) = lo;
+        *reinterpret_cast<u32x4*>(vst + vr * ROWB + (((c + 1) ^ swz_v16(vr)) << 4)) = hi;
+      }
+      // K: widen into the A fragments
+      bf16x8 kf[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float skk = scale_of(r.ek[hh]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint2 u = r.k[4 * hh + c];
+          u32x4 kw;
+          kw[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.x, skk, false));
+          kw[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.x, skk, true));
+          kw[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.y, skk, false));
+          kw[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.y, skk, true));
+          kf[4 * hh + c] = __builtin_bit_cast(bf16x8, kw);
+        }
+      }
+      compute_block(b, kf, 0);
+    };
+    Raw r0, r1;
+    int b = wave;
+    if (b < nblk) load_raw(b, r0);
+    if (tree) tree_prep_lds_from(parent_i, p.N, anc, par, jmp, p.dev_error);
+    for (; b < nblk; b += 16) {
+      if (b + 8 < nblk) load_raw(b + 8, r1);
+      compute_raw(b, r0);
+      if (b + 8 >= nblk) break;
+      if (b + 16 < nblk) load_raw(b + 16, r0);
+      compute_raw(b + 8, r1);
     }
-    compute_block(b + 8, kf1, 1);
+    if (__any(bad_exp) && lane == 0 && p.dev_error) *p.dev_error = TV_ERR_INVALID_ARG;
   }
 
   // ---- the eight waves' states meet in LDS (the V stages are free after the barrier):
@@ -1477,11 +1570,18 @@ hipError_t launch_attn(const AttnPlan& plan, bool f8, const void* q, const void*
   sp.remap = (nwg % 8 == 0) ? 1 : 0;
 
   hipError_t e;
-  if (!f8 && plan.M <= 16) {
+  if (plan.M <= 16 && !f8) {
     static std::atomic<uint64_t> attr_devices{0};
-    e = allow_dynamic_lds(&attn_rows16_kernel, R16_SMEM_BYTES, attr_devices);
+    e = allow_dynamic_lds(&attn_rows16_kernel<false>, R16_SMEM_BYTES, attr_devices);
     if (e == hipSuccess) {
-      hipLaunchKernelGGL(attn_rows16_kernel, dim3(nwg), dim3(512), R16_SMEM_BYTES, stream, sp);
+      hipLaunchKernelGGL(attn_rows16_kernel<false>, dim3(nwg), dim3(512), R16_SMEM_BYTES, stream, sp);
+      e = hipGetLastError();
+    }
+  } else if (plan.M <= 16) {
+    static std::atomic<uint64_t> attr_devices{0};
+    e = allow_dynamic_lds(&attn_rows16_kernel<true>, R16_SMEM_BYTES, attr_devices);
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL(attn_rows16_kernel<true>, dim3(nwg), dim3(512), R16_SMEM_BYTES, stream, sp);
       e = hipGetLastError();
     }
   } else if (f8) {

@@ -212,9 +212,9 @@ def test_fp8_attention_forced_splits(splits):
     _check_fp8_workload(make("budget22", 11, L=7000, N=22), f"splits={splits}", num_splits=splits)
 
 
-# One row-wave: each wave streams and widens its own blocks. T = 5001 keys: the requests
-# give 1, 4, 40 and 79 splits of 158, 40, 4 and 2 blocks, so with few blocks most waves
-# have none, and the last block is cut by the end of the keys.
+# Eight stacked rows (the 16-row kernel): each wave streams and widens its own blocks.
+# T = 5001 keys: the requests give 1, 4, 40 and 79 splits of 158, 40, 4 and 2 blocks, so
+# with few blocks most waves have none, and the last block is cut by the end of the keys.
 @pytest.mark.parametrize("splits", [1, 4, 40, 1024])
 def test_fp8_attention_single_row_wave_splits(splits):
     _check_fp8_workload(make("decode_1node", 3, L=5000), f"decode splits={splits}", num_splits=splits)
@@ -226,6 +226,38 @@ def test_fp8_attention_single_row_wave_splits(splits):
 @pytest.mark.parametrize("L,splits", [(700, 12), (700, 6), (700, 4), (700, 3), (700, 2), (700, 1), (1200, 4)])
 def test_fp8_attention_dense_short_splits(L, splits):
     _check_fp8_workload(make("branch_8k", 4, L=L), f"8x1 L={L} splits={splits}", num_splits=splits)
+
+
+# At most 16 stacked rows: the 16-row kernel with K widened in registers and V widened
+# into each wave's stage (the same shapes as the bf16 16-row cases); then 17-32 rows, the
+# single-row-wave kernel with its own widening.
+FP8_ROWS16 = [
+    ("chain16_G1", dict(L=1000, N=16, tree="chain", Hq=8, Hkv=8)),
+    ("N4_G4", dict(L=2500, N=4, tree="random16", Hq=16, Hkv=4)),
+    ("N2_G8_L0", dict(L=0, N=2, tree="chain", Hq=8, Hkv=1)),
+    ("N11_G1_L31", dict(L=31, N=11, tree="random16", Hq=3, Hkv=3)),
+    ("N3_G5_L96", dict(L=96, N=3, tree="random16", Hq=10, Hkv=2)),
+    ("N1_G8_peaky", dict(L=20000, N=1, tree="chain", Hq=8, Hkv=1, peaky=True)),
+    ("N2_G6_peaky", dict(L=9000, N=2, tree="chain", Hq=24, Hkv=4, peaky=True)),
+]
+FP8_ROWS32 = [
+    ("N3_G8", dict(L=500, N=3, tree="random16", Hq=8, Hkv=1)),
+    ("N17_G1", dict(L=3000, N=17, tree="random16", Hq=4, Hkv=4)),
+]
+
+
+@pytest.mark.parametrize("label,ov", FP8_ROWS16, ids=[e[0] for e in FP8_ROWS16])
+def test_fp8_attention_rows16(label, ov):
+    w = make("budget22", 13, **ov)
+    assert w.N * w.Hq // w.Hkv <= 16
+    _check_fp8_workload(w, f"16-row {label}")
+
+
+@pytest.mark.parametrize("label,ov", FP8_ROWS32, ids=[e[0] for e in FP8_ROWS32])
+def test_fp8_attention_rows17_to_32(label, ov):
+    w = make("budget22", 14, **ov)
+    assert 16 < w.N * w.Hq // w.Hkv <= 32
+    _check_fp8_workload(w, f"single-row-wave {label}")
 
 
 def test_fp8_attention_peaky_keys():
