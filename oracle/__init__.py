@@ -7,9 +7,14 @@ its binding never do, and this package imports nothing from them.
 
 from .kvquant import (  # noqa: F401
     dequantize_kv,
+    dequantize_kv_mx4,
+    e2m1_decode,
+    e2m1_encode,
     e4m3_decode,
     e4m3_encode,
+    mx4_block_exponent,
     quantize_kv,
+    quantize_kv_mx4,
     row_scale_exponent,
 )
 from .sampling import philox4x32_10, sample_accept, sample_rows, uniforms  # noqa: F401

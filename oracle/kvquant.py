@@ -101,3 +101,93 @@ def quantize_kv(bits, chunk_rows: int = 1 << 16) -> tuple[np.ndarray, np.ndarray
 def dequantize_kv(codes, exps) -> np.ndarray:
     """float64 [T, H, D] = code value * 2^exponent."""
     return np.ldexp(e4m3_decode(codes), np.asarray(exps, dtype=np.int64)[..., None])
+
+
+# ---------------------------------------------------------------- 4-bit (MX-style) cache
+#
+# A sub-8-bit cache in the block structure of the OCP Microscaling (MX) formats: blocks of
+# 32 consecutive values of a row share one power-of-two scale, and each value is an OCP
+# FP4 E2M1 element (1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit; magnitudes
+# 0, 0.5, 1, 1.5, 2, 3, 4, 6; no infinities or NaN). Self-defined where the pages are
+# silent, and exact where it matters:
+#
+# * Scale: per block the smallest 2^e with max|x| <= 6 * 2^e (2^0 for an all-zero block),
+#   clamped to e in [-125, 125] (so that every element value times 2^e is a finite bf16
+#   and 2^e a normal float32). The MX specification instead takes floor(log2 max|x|) - 2
+#   and lets the largest elements clip; the smallest scale that fits clips nothing.
+# * Element: x * 2^-e (exact) rounded to the nearest E2M1 value, ties to the even code
+#   (mantissa bit 0); magnitudes above 6 (possible only where e was clamped) saturate to 6;
+#   a negative value that rounds to zero is coded +0.
+# * Packing: element 2j of a row in the low nibble of byte j, element 2j + 1 in the high
+#   nibble; scales as int8 exponents [T, H, D / 32].
+# * Dequantisation: decode(code) * 2^e, exactly representable in bfloat16.
+
+MX4_BLOCK = 32
+E2M1_MAX = 6.0
+MX4_EXP_MIN = -125
+MX4_EXP_MAX = 125
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """float64 values of E2M1 codes (integers 0 .. 15)."""
+    c = np.asarray(codes, dtype=np.int64)
+    s = np.where(c & 0x8, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = c & 0x1
+    val = np.where(e == 0, m * 0.5, (1 + m / 2.0) * 2.0 ** (e - 1))
+    return s * val
+
+
+def e2m1_encode(y) -> np.ndarray:
+    """Nearest E2M1 code (uint8 0 .. 15) of float64 values, ties to the even code,
+    saturating at +-6; -0 and negative values rounding to zero give code 0.
+
+    Written as a search over the eight non-negative code values: the nearest wins, at an
+    exact midpoint the code with mantissa bit 0."""
+    y = np.asarray(y, dtype=np.float64)
+    if np.any(~np.isfinite(y)):
+        raise ValueError("values must be finite")
+    codes = np.arange(8, dtype=np.uint8)
+    vals = e2m1_decode(codes)
+    a = np.minimum(np.abs(y).ravel(), E2M1_MAX)
+    d = np.abs(vals[None, :] - a[:, None])                   # distance to every value
+    best = d.min(axis=1, keepdims=True)
+    tied = d == best
+    even = tied & ((codes[None, :] & 1) == 0)
+    pick = np.where(even.any(axis=1), even.argmax(axis=1), tied.argmax(axis=1)).astype(np.uint8)
+    sign = (y.ravel() < 0) & (pick != 0)
+    return (pick | np.where(sign, 0x8, 0).astype(np.uint8)).reshape(y.shape)
+
+
+def mx4_block_exponent(amax: float) -> int:
+    """Smallest e with amax <= 6 * 2^e (0 for amax == 0), clamped to [-125, 125]; by exact
+    exponent arithmetic (6 = 0.75 * 2^3)."""
+    if amax == 0:
+        return 0
+    m, k = math.frexp(amax)            # amax = m * 2^k, 0.5 <= m < 1
+    e = k - 3 if m <= 0.75 else k - 2
+    return min(max(e, MX4_EXP_MIN), MX4_EXP_MAX)
+
+
+def quantize_kv_mx4(bits) -> tuple[np.ndarray, np.ndarray]:
+    """bf16 bits [T, H, D] -> (packed E2M1 codes uint8 [T, H, D / 2], block exponents int8
+    [T, H, D / 32]). Each block is scaled by 2^-e (exact) and encoded."""
+    bits = np.asarray(bits)
+    T, H, D = bits.shape
+    x = bf16_bits_to_f64(bits).reshape(T, H, D // MX4_BLOCK, MX4_BLOCK)
+    amax = np.abs(x).max(axis=3)
+    exps = np.vectorize(mx4_block_exponent, otypes=[np.int64])(amax) if amax.size else np.zeros(amax.shape, np.int64)
+    codes = e2m1_encode(np.ldexp(x, -exps[..., None])).reshape(T, H, D)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return packed, exps.astype(np.int8)
+
+
+def dequantize_kv_mx4(packed, exps) -> np.ndarray:
+    """float64 [T, H, D] = decode(code) * 2^(exponent of its block)."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    T, H, D2 = packed.shape
+    codes = np.empty((T, H, 2 * D2), dtype=np.uint8)
+    codes[..., 0::2] = packed & 0xF
+    codes[..., 1::2] = packed >> 4
+    e = np.repeat(np.asarray(exps, dtype=np.int64), MX4_BLOCK, axis=2)
+    return np.ldexp(e2m1_decode(codes), e)
