@@ -19,6 +19,7 @@ from .tv import (  # noqa: F401
     argmax_workspace_size,
     kv_commit,
     kv_quantize_fp8,
+    kv_quantize_mx4,
     lib,
     sample_accept,
     status_string,

@@ -251,4 +251,19 @@ int tv_kv_quantize_fp8(const void* src, int64_t src_stride_t, int64_t src_stride
                                           codes_stride_h, exps, static_cast<hipStream_t>(stream)));
 }
 
+int tv_kv_quantize_mx4(const void* src, int64_t src_stride_t, int64_t src_stride_h, int T, int Hkv, int D,
+                       void* codes, int64_t codes_stride_t, int64_t codes_stride_h, int8_t* exps, void* stream) {
+  if (!src || !codes || !exps) return TV_ERR_INVALID_ARG;
+  if (T < 0 || Hkv < 1 || (int64_t)T * Hkv > INT32_MAX / 4) return TV_ERR_INVALID_ARG;
+  if (D != TV_HEAD_DIM) return TV_ERR_UNSUPPORTED;
+  if (src_stride_t < (int64_t)Hkv * D || src_stride_h < D || src_stride_t % 8 || src_stride_h % 8)
+    return TV_ERR_INVALID_ARG;
+  if (codes_stride_t < (int64_t)Hkv * D / 2 || codes_stride_h < D / 2 || codes_stride_t % 16 || codes_stride_h % 16)
+    return TV_ERR_INVALID_ARG;
+  if (!aligned16(src) || !aligned16(codes)) return TV_ERR_INVALID_ARG;
+  if (T == 0) return TV_OK;
+  return status_of(tv::launch_kv_quantize_mx4(src, src_stride_t, src_stride_h, T, Hkv, codes, codes_stride_t,
+                                              codes_stride_h, exps, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

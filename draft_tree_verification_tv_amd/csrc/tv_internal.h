@@ -176,6 +176,8 @@ hipError_t launch_sample_accept(const void* logits, int dtype, int N, int V, int
                                 uint64_t seed, uint64_t offset, const int32_t* parent, const int32_t* draft,
                                 int32_t* tok, int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
                                 int32_t* bonus, void* workspace, int32_t* dev_error, hipStream_t stream);
+hipError_t launch_kv_quantize_mx4(const void* src, int64_t st, int64_t sh, int T, int H, void* codes, int64_t cst,
+                                  int64_t csh, int8_t* exps, hipStream_t stream);
 hipError_t launch_kv_quantize(const void* src, int64_t st, int64_t sh, int T, int H, void* codes, int64_t cst,
                               int64_t csh, int32_t* exps, hipStream_t stream);
 hipError_t launch_kv_commit(void* k, void* v, int64_t st, int64_t sh, int Hkv, int D, int L, int N,

@@ -26,7 +26,7 @@ HEAD_DIM = 128
 EXPORTS = ("tv_abi_version", "tv_status_string", "tv_validate_tree_host", "tv_tree_prep",
            "tv_tree_attn_workspace_size", "tv_tree_attn", "tv_argmax_workspace_size",
            "tv_argmax", "tv_accept", "tv_argmax_accept", "tv_sample_accept", "tv_kv_commit",
-           "tv_kv_quantize_fp8", "tv_tree_attn_fp8", "tv_tree_attn_noalloc")
+           "tv_kv_quantize_fp8", "tv_tree_attn_fp8", "tv_tree_attn_noalloc", "tv_kv_quantize_mx4")
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
@@ -88,6 +88,8 @@ def lib():
                                        _i32, _vp, _vp, _vp, _sz, _vp, _vp]
         L.tv_kv_quantize_fp8.restype = _i32
         L.tv_kv_quantize_fp8.argtypes = [_vp, _i64, _i64, _i32, _i32, _i32, _vp, _i64, _i64, _vp, _vp]
+        L.tv_kv_quantize_mx4.restype = _i32
+        L.tv_kv_quantize_mx4.argtypes = [_vp, _i64, _i64, _i32, _i32, _i32, _vp, _i64, _i64, _vp, _vp]
         if L.tv_abi_version() != 1:
             raise RuntimeError("libtv ABI version mismatch")
         _lib = L
@@ -506,6 +508,37 @@ def kv_quantize_fp8(x, codes=None, exps=None, stream=None):
         raise ValueError("codes must have a contiguous last dim")
     _check(lib().tv_kv_quantize_fp8(_ptr(x), x.stride(0), x.stride(1), T, H, D, _ptr(codes), codes.stride(0),
                                     codes.stride(1), _ptr(exps), _stream(stream)), "tv_kv_quantize_fp8")
+    return codes, exps
+
+
+def kv_quantize_mx4(x, codes=None, exps=None, stream=None):
+    """Quantise a bf16 cache x [T, Hkv, D] (last dim contiguous) to 4-bit E2M1 codes, two
+    per byte (uint8 [T, Hkv, D / 2]; value 2j in the low nibble of byte j), and one
+    power-of-two exponent per 32-value block (int8 [T, Hkv, D / 32], contiguous); a block
+    dequantises to code * 2^exp. Returns (codes, exps)."""
+    _need_cuda("x", x, torch.bfloat16)
+    if x.dim() != 3 or (x.numel() and x.stride(2) != 1):
+        raise ValueError("x must be [T, Hkv, D] with a contiguous last dim")
+    T, H, D = x.shape
+    if D % 32:
+        raise ValueError("D must be a multiple of 32")
+    if codes is None:
+        codes = torch.empty((T, H, D // 2), dtype=torch.uint8, device=x.device)
+    if exps is None:
+        exps = torch.empty((T, H, D // 32), dtype=torch.int8, device=x.device)
+    _need_cuda("codes", codes, torch.uint8)
+    _need_cuda("exps", exps, torch.int8)
+    if tuple(codes.shape) != (T, H, D // 2) or tuple(exps.shape) != (T, H, D // 32) or not exps.is_contiguous():
+        raise ValueError("codes must be [T, Hkv, D / 2] (contiguous last dim), exps a contiguous [T, Hkv, D / 32]")
+    for t in (codes, exps):
+        if t.device != x.device:
+            raise ValueError("x, codes and exps must be on one device")
+    if T == 0:
+        return codes, exps
+    if codes.stride(2) != 1:
+        raise ValueError("codes must have a contiguous last dim")
+    _check(lib().tv_kv_quantize_mx4(_ptr(x), x.stride(0), x.stride(1), T, H, D, _ptr(codes), codes.stride(0),
+                                    codes.stride(1), _ptr(exps), _stream(stream)), "tv_kv_quantize_mx4")
     return codes, exps
 
 

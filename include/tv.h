@@ -21,6 +21,7 @@
  *   tv_sample_accept   the same with sampled targets (temperature > 0)
  *   tv_kv_commit  moves the accepted nodes' K/V rows behind the context   (bit exact)
  *   tv_kv_quantize_fp8   bf16 cache -> FP8 (E4M3) codes + per-row scales      (bit exact)
+ *   tv_kv_quantize_mx4   bf16 cache -> 4-bit (E2M1) codes + per-32 scales     (bit exact)
  *   tv_tree_attn_fp8     tree attention over that FP8 cache
  *
  * Conventions shared by every call
@@ -273,6 +274,28 @@ int tv_kv_commit(void* k, void* v, int64_t kv_stride_t, int64_t kv_stride_h, int
 int tv_kv_quantize_fp8(const void* src, int64_t src_stride_t, int64_t src_stride_h, int T,
                        int Hkv, int D, void* codes, int64_t codes_stride_t,
                        int64_t codes_stride_h, int32_t* exps, void* stream);
+
+/*
+ * 4-bit key/value cache: quantiser. A quantised cache of under 8 bits per value, as the
+ * pages' 256K-context cache is (Lucebox-Hub review, section "2. DFlash"); the format is
+ * this library's own, in the block structure of the OCP Microscaling formats: each run of
+ * 32 consecutive values of a (token, head) row shares one exponent e, the smallest integer
+ * with max|x| <= 6 * 2^e (e = 0 for an all-zero block) clamped to [-125, 125], and each
+ * value becomes the OCP FP4 E2M1 code (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) nearest to
+ * x * 2^-e, ties to the even code, saturating at 6 (only where e was clamped), -0 coded
+ * as +0. The block dequantises to decode(code) * 2^e, which is exact in bfloat16.
+ *   src          bf16 [T][Hkv][D], strides src_stride_t / src_stride_h in elements
+ *                (multiples of 8), D contiguous; 16-byte aligned. Values must be finite.
+ *   codes        uint8 [T][Hkv][D / 2] out, two codes per byte (value 2j in the low
+ *                nibble of byte j), strides codes_stride_t / codes_stride_h in bytes
+ *                (multiples of 16), D / 2 contiguous; 16-byte aligned.
+ *   exps         int8 [T * Hkv * D / 32] out (block b of row (t, h) at (t * Hkv + h) * 4 + b).
+ * Limits: T >= 0 (T = 0 enqueues nothing), Hkv >= 1, D = TV_HEAD_DIM (else
+ * TV_ERR_UNSUPPORTED), strides at least the packed ones.
+ */
+int tv_kv_quantize_mx4(const void* src, int64_t src_stride_t, int64_t src_stride_h, int T,
+                       int Hkv, int D, void* codes, int64_t codes_stride_t,
+                       int64_t codes_stride_h, int8_t* exps, void* stream);
 
 #ifdef __cplusplus
 }

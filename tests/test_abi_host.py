@@ -250,6 +250,29 @@ def test_kv_quantize_rejects(args, status):
     assert tv.lib().tv_kv_quantize_fp8(*args, None) == status
 
 
+# tv_kv_quantize_mx4(src, sst, ssh, T, Hkv, D, codes, cst, csh, exps, stream): codes rows
+# of D / 2 bytes, strides multiples of 16, 16-byte aligned codes; exps int8 (any alignment)
+@pytest.mark.parametrize("args,status", [
+    ((None, 1024, 128, 10, 8, 128, FAKE, 512, 64, FAKE), 1),
+    ((FAKE, 1024, 128, 10, 8, 128, None, 512, 64, FAKE), 1),
+    ((FAKE, 1024, 128, 10, 8, 128, FAKE, 512, 64, None), 1),
+    ((FAKE, 1024, 128, -1, 8, 128, FAKE, 512, 64, FAKE), 1),
+    ((FAKE, 1024, 128, 10, 0, 128, FAKE, 512, 64, FAKE), 1),
+    ((FAKE, 1024, 128, 10, 8, 64, FAKE, 512, 64, FAKE), 3),
+    ((FAKE, 1022, 128, 10, 8, 128, FAKE, 512, 64, FAKE), 1),
+    ((FAKE, 1024, 128, 10, 8, 128, FAKE, 496, 64, FAKE), 1),     # codes row stride below 8 heads
+    ((FAKE, 1024, 128, 10, 8, 128, FAKE, 512, 48, FAKE), 1),     # head stride below D / 2
+    ((FAKE, 1024, 128, 10, 8, 128, FAKE, 520, 64, FAKE), 1),     # not a multiple of 16
+    ((FAKE, 1024, 128, 10, 8, 128, FAKE, 512, 72, FAKE), 1),
+    ((ctypes.c_void_p(0x10008), 1024, 128, 10, 8, 128, FAKE, 512, 64, FAKE), 1),
+    ((FAKE, 1024, 128, 10, 8, 128, ctypes.c_void_p(0x10008), 512, 64, FAKE), 1),
+    ((FAKE, 1 << 40, 128, 1 << 30, 8, 128, FAKE, 1 << 40, 64, FAKE), 1),
+    ((FAKE, 1024, 128, 0, 8, 128, FAKE, 512, 64, ctypes.c_void_p(0x10003)), 0),
+])
+def test_kv_quantize_mx4_rejects(args, status):
+    assert tv.lib().tv_kv_quantize_mx4(*args, None) == status
+
+
 PROBE_HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "tv_probe.h")
 
 
