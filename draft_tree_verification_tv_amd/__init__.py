@@ -20,6 +20,7 @@ from .tv import (  # noqa: F401
     kv_commit,
     kv_quantize_fp8,
     kv_quantize_mx4,
+    tree_attn_mx4,
     lib,
     sample_accept,
     status_string,

@@ -167,6 +167,31 @@ int tv_tree_attn_fp8(const void* q, const void* k_codes, const void* v_codes, co
                                             static_cast<hipStream_t>(stream)));
 }
 
+int tv_tree_attn_mx4(const void* q, const void* k_codes, const void* v_codes, const int8_t* k_exps,
+                     const int8_t* v_exps, int64_t kv_stride_t, int64_t kv_stride_h, const int32_t* parent,
+                     int N, int L, int Hq, int Hkv, int D, float scale, int num_splits, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream) {
+  if (!q || !k_codes || !v_codes || !k_exps || !v_exps || !parent || !out) return TV_ERR_INVALID_ARG;
+  if (!attn_args_ok(N, L, Hq, Hkv, num_splits)) return TV_ERR_INVALID_ARG;
+  if (D != TV_HEAD_DIM) return TV_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return TV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(out)) return TV_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(k_exps) & 3u) || (reinterpret_cast<uintptr_t>(v_exps) & 3u))
+    return TV_ERR_INVALID_ARG;
+  if (kv_stride_t < 0 || kv_stride_h < 0 || kv_stride_t % 16 || kv_stride_h % 16) return TV_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return TV_ERR_INVALID_ARG;
+  // One KV head's code rows and the exponent words must be addressable with 32-bit byte
+  // offsets.
+  if (((int64_t)L + N) * kv_stride_t + 4096 > (int64_t)UINT32_MAX) return TV_ERR_UNSUPPORTED;
+  if (((int64_t)L + N) * Hkv * 4 > (int64_t)UINT32_MAX) return TV_ERR_UNSUPPORTED;
+  const tv::AttnPlan p = tv::attn_plan(N, L, Hq, Hkv, num_splits, cu_count());
+  const size_t need = tv::attn_workspace_bytes(p, Hkv);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return TV_ERR_WORKSPACE;
+  return status_of(tv::launch_tree_attn_mx4(p, q, k_codes, v_codes, k_exps, v_exps, kv_stride_t, kv_stride_h,
+                                            parent, N, L, Hq, Hkv, scale, out, lse, workspace, dev_error,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 size_t tv_argmax_workspace_size(int N, int V) {
   if (N < 1 || V < 1 || V >= INT32_MAX) return 0;
   return tv::argmax_workspace_bytes(N, V);

@@ -58,6 +58,7 @@
 //     V, inside the same one-barrier-per-tile pipeline. The MFMA and softmax code is
 //     shared with the bf16 kernel, so both compute the same function of the bf16 values.
 #include <atomic>
+#include <type_traits>
 #include <cmath>
 
 #include "tv_internal.h"
@@ -94,6 +95,13 @@ static_assert(F8_SMEM_BYTES <= 160 * 1024, "FP8 stages exceed the LDS");
 // fp32: smallest code 2^-9, largest 448.
 constexpr int kExpMin = -117;
 constexpr int kExpMax = 119;
+// 4-bit cache (E2M1 codes, one int8 exponent per 32 values): raw stages of [K codes 4 KB]
+// [V codes 4 KB][K exponents 256 B][V exponents 256 B] inside the FP8 raw-stage stride; an
+// exponent e in [-125, 125] keeps every code * 2^e a finite bf16 and 2^e a normal float.
+constexpr int MX_ROWB = D / 2;                              // code bytes per row
+constexpr int MX_TILE_B = KT * MX_ROWB;                     // 4 KB
+constexpr int kMxExpMin = -125;
+constexpr int kMxExpMax = 125;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kCheck = 256.0f;  // largest probability (and 16-key partial sum) kept
@@ -180,16 +188,18 @@ __device__ __forceinline__ void barrier_keep(void) {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(kPending) : "memory");
 }
 
-template <int RWV, int KSW, bool kF8>
+template <int RWV, int KSW, bool kF8, bool kMX = false>
 __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams p) {
   constexpr int NW = RWV * KSW;
   constexpr int ROWS = RWV * 32;  // stacked rows per workgroup
   static_assert(NW == 8, "eight waves per workgroup");
+  static_assert(!kMX || (kF8 && RWV == 8), "the 4-bit cache runs the 256-row kernel");
   // Copies per wave per tile: bf16, 16 blocks of 1 KB for each of K and V; FP8, 8 blocks
-  // of codes for each plus one copy of 128 / NW exponents.
+  // of codes for each plus one copy of 128 / NW exponents; 4-bit, one of the 4 + 4 code
+  // blocks plus one copy of 16 exponent words.
   constexpr int BLK = kF8 ? KT / 8 : KT / 4;
   constexpr int BPW = BLK / NW;
-  constexpr int DPT = 2 * BPW + (kF8 ? 1 : 0);
+  constexpr int DPT = kMX ? 2 : 2 * BPW + (kF8 ? 1 : 0);
   constexpr int EPW = 2 * KT / NW;      // FP8: exponents copied per wave
   constexpr int TREE_OFF = kF8 ? F8_TREE_OFF : NSTAGE * STAGE_B;
   static_assert(BLK % NW == 0, "waves must divide the tile");
@@ -343,8 +353,26 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
       }
     }
   };
+  // 4-bit: wave w copies code block w % 4 (16 rows x 64 bytes; lane i: row 16 (w % 4) +
+  // i / 4, 16-byte chunk i % 4) of K (w < 4) or V, and 16 exponent words (4 int8 per row)
+  // as the FP8 path copies its exponents. Rows past L + N repeat row L + N - 1.
+  const char* cbase = nullptr;
+  if constexpr (kMX) cbase = uniform_ptr(wave < NW / 2 ? kb8 : vb8);
+  auto issue_mx = [&](int t) __attribute__((always_inline)) {
+    const int kt0 = kbeg + t * KT;
+    const uint32_t raw = lds_base + (uint32_t)((t & (F8_NRAW - 1)) * F8_RAW_B);
+    const int row = 16 * (wave & 3) + (lane >> 2);
+    const uint32_t off = (uint32_t)min(kt0 + row, p.T - 1) * rowstride_b + (uint32_t)((lane & 3) << 4);
+    dma16(raw + (uint32_t)((wave >> 2) * MX_TILE_B + (wave & 3) * 1024), off, cbase);
+    if (lane < EPW) {
+      const uint32_t key = (uint32_t)min(kt0 + ekey, p.T - 1);
+      dma4(raw + 2 * MX_TILE_B + wave * EPW * 4, (key * (uint32_t)p.Hkv + (uint32_t)h) * 4u, ebase);
+    }
+  };
   auto issue = [&](int t) __attribute__((always_inline)) {
-    if constexpr (kF8)
+    if constexpr (kMX)
+      issue_mx(t);
+    else if constexpr (kF8)
       issue_f8(t);
     else
       issue_bf16(t);
@@ -556,7 +584,37 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
   // chunks to their swizzled places. Exponents outside [kExpMin, kExpMax] are clamped and
   // reported.
   bool bad_exp = false;
+  // 4-bit: thread i widens 16 codes (row i/8, dims 16*(i%8) .., 8 bytes) with their
+  // block's scale 2^e (byte (i%8)/2 of the row's exponent word) into the same two chunks.
+  auto widen_mx = [&](int t, bool is_v) __attribute__((always_inline)) {
+    const char* raw = smem + (t & (F8_NRAW - 1)) * F8_RAW_B + (is_v ? MX_TILE_B : 0);
+    const uint32_t* ex = reinterpret_cast<const uint32_t*>(smem + (t & (F8_NRAW - 1)) * F8_RAW_B + 2 * MX_TILE_B) +
+                         (is_v ? KT : 0);
+    char* dst = const_cast<char*>(is_v ? vstage(t) + VBASE : kstage(t));
+    const int row = tid >> 3, c8 = tid & 7;
+    const uint2 w = *reinterpret_cast<const uint2*>(raw + row * MX_ROWB + c8 * 8);
+    int e = (int)(int8_t)(uint8_t)(ex[row] >> (8 * (c8 >> 1)));
+    bad_exp |= e < kMxExpMin || e > kMxExpMax;
+    e = min(max(e, kMxExpMin), kMxExpMax);
+    const float sc = __int_as_float((e + 127) << 23);
+    u32x4 lo, hi;
+    lo[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w.x, sc, 0));
+    lo[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w.x, sc, 1));
+    lo[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w.x, sc, 2));
+    lo[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w.x, sc, 3));
+    hi[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w.y, sc, 0));
+    hi[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w.y, sc, 1));
+    hi[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w.y, sc, 2));
+    hi[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w.y, sc, 3));
+    const int sw = is_v ? swz_v(row) : swz_k(row);
+    *reinterpret_cast<u32x4*>(dst + row * ROWB + (((2 * c8) ^ sw) << 4)) = lo;
+    *reinterpret_cast<u32x4*>(dst + row * ROWB + (((2 * c8 + 1) ^ sw) << 4)) = hi;
+  };
   auto widen = [&](int t, bool is_v) __attribute__((always_inline)) {
+    if constexpr (kMX) {
+      widen_mx(t, is_v);
+      return;
+    }
     const char* raw = smem + (t & (F8_NRAW - 1)) * F8_RAW_B + (is_v ? F8_TILE_B : 0);
     const int* ex = reinterpret_cast<const int*>(smem + (t & (F8_NRAW - 1)) * F8_RAW_B + 2 * F8_TILE_B) +
                     (is_v ? KT : 0);
@@ -1041,7 +1099,7 @@ constexpr int R16_TREE_OFF = 8 * R16_STAGES * R16_VB;
 constexpr int R16_SMEM_BYTES = R16_TREE_OFF + TREE_BYTES;
 static_assert(R16_SMEM_BYTES <= 160 * 1024, "16-row kernel LDS");
 
-template <bool kF8>
+template <bool kF8, bool kMX = false>
 __global__ __launch_bounds__(512) void attn_rows16_kernel(SplitParams p) {
   constexpr int NW = 8;
   extern __shared__ __align__(16) char smem[];
@@ -1244,13 +1302,70 @@ __global__ __launch_bounds__(512) void attn_rows16_kernel(SplitParams p) {
       e = min(max(e, kExpMin), kExpMax);
       return __int_as_float((e + 127) << 23);
     };
-    struct Raw {
+    struct RawF8 {
       uint2 k[8];
       int ek[2];
       u32x4 v[4];
       int ev;
     };
-    auto load_raw = [&](int b, Raw& r) __attribute__((always_inline)) {
+    // 4-bit: K 8 codes (4 bytes) per fragment and the key's word of 4 block exponents;
+    // V 64 codes (32 bytes) of row vr and that row's exponent word.
+    struct RawMX {
+      uint32_t k[8];
+      uint32_t ek[2];
+      u32x4 v[2];
+      uint32_t ev;
+    };
+    using Raw = std::conditional_t<kMX, RawMX, RawF8>;
+    auto mx_scale = [&](uint32_t word, int b) __attribute__((always_inline)) -> float {
+      int e = (int)(int8_t)(uint8_t)(word >> (8 * b));
+      bad_exp |= e < kMxExpMin || e > kMxExpMax;
+      e = min(max(e, kMxExpMin), kMxExpMax);
+      return __int_as_float((e + 127) << 23);
+    };
+    auto cvt4 = [&](uint32_t w, float sc) __attribute__((always_inline)) -> u32x4 {
+      return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3))};
+    };
+    auto load_raw_mx = [&](int b, RawMX& r) __attribute__((always_inline)) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int key = min(kbeg + b * 32 + 16 * hh + i16, p.T - 1);
+        const char* row = kb8 + (uint32_t)key * rowstride_b + g * 4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) r.k[4 * hh + c] = *reinterpret_cast<const uint32_t*>(row + c * 16);
+        r.ek[hh] = (uint32_t)ekp[(int64_t)key * p.Hkv + h];
+      }
+      const int kv = min(kbeg + b * 32 + vr, p.T - 1);
+      const char* vrow = vb8 + (uint32_t)kv * rowstride_b + vh * 32;
+      r.v[0] = *reinterpret_cast<const u32x4*>(vrow);
+      r.v[1] = *reinterpret_cast<const u32x4*>(vrow + 16);
+      r.ev = (uint32_t)evp[(int64_t)kv * p.Hkv + h];
+    };
+    auto compute_raw_mx = [&](int b, const RawMX& r) __attribute__((always_inline)) {
+      // V: dims 64 vh + 32 j + 8 q .. + 7 (block 2 vh + j) become logical chunk 8 vh + 4 j + q
+      char* vst = smem + wave * R16_STAGES * R16_VB;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float sv = mx_scale(r.ev, 2 * vh + j);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = 8 * vh + 4 * j + q;
+          *reinterpret_cast<u32x4*>(vst + vr * ROWB + ((c ^ swz_v16(vr)) << 4)) = cvt4(r.v[j][q], sv);
+        }
+      }
+      // K: fragment (hh, c) holds dims 32 c + 8 g .. + 7 of key 16 hh + i16 (block c)
+      bf16x8 kf[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          kf[4 * hh + c] = __builtin_bit_cast(bf16x8, cvt4(r.k[4 * hh + c], mx_scale(r.ek[hh], c)));
+      compute_block(b, kf, 0);
+    };
+    auto load_raw_f8 = [&](int b, RawF8& r) __attribute__((always_inline)) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int key = min(kbeg + b * 32 + 16 * hh + i16, p.T - 1);
@@ -1265,7 +1380,7 @@ __global__ __launch_bounds__(512) void attn_rows16_kernel(SplitParams p) {
       for (int j = 0; j < 4; ++j) r.v[j] = *reinterpret_cast<const u32x4*>(vrow + j * 16);
       r.ev = evp[(int64_t)kv * p.Hkv + h];
     };
-    auto compute_raw = [&](int b, const Raw& r) __attribute__((always_inline)) {
+    auto compute_raw_f8 = [&](int b, const RawF8& r) __attribute__((always_inline)) {
       // V: widen 64 codes of row vr and write them as logical chunks 8 vh .. 8 vh + 7
       char* vst = smem + wave * R16_STAGES * R16_VB;
       const float svv = scale_of(r.ev);
@@ -1301,6 +1416,18 @@ __global__ __launch_bounds__(512) void attn_rows16_kernel(SplitParams p) {
         }
       }
       compute_block(b, kf, 0);
+    };
+    auto load_raw = [&](int b, Raw& r) __attribute__((always_inline)) {
+      if constexpr (kMX)
+        load_raw_mx(b, r);
+      else
+        load_raw_f8(b, r);
+    };
+    auto compute_raw = [&](int b, const Raw& r) __attribute__((always_inline)) {
+      if constexpr (kMX)
+        compute_raw_mx(b, r);
+      else
+        compute_raw_f8(b, r);
     };
     Raw r0, r1;
     int b = wave;
@@ -1483,14 +1610,14 @@ hipError_t allow_dynamic_lds(Kernel kernel, int bytes, std::atomic<uint64_t>& do
   return hipSuccess;
 }
 
-template <int RWV, bool kF8>
+template <int RWV, bool kF8, bool kMX = false>
 hipError_t launch_split(const SplitParams& sp, int nwg, hipStream_t stream) {
   constexpr int KSW = 8 / RWV;
   constexpr int smem = kF8 ? F8_SMEM_BYTES : SMEM_BYTES;
   static std::atomic<uint64_t> attr_devices{0};
-  hipError_t e = allow_dynamic_lds(&attn_split_kernel<RWV, KSW, kF8>, smem, attr_devices);
+  hipError_t e = allow_dynamic_lds(&attn_split_kernel<RWV, KSW, kF8, kMX>, smem, attr_devices);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_split_kernel<RWV, KSW, kF8>), dim3(nwg), dim3(512), smem, stream, sp);
+  hipLaunchKernelGGL((attn_split_kernel<RWV, KSW, kF8, kMX>), dim3(nwg), dim3(512), smem, stream, sp);
   return hipGetLastError();
 }
 
@@ -1534,7 +1661,11 @@ size_t attn_workspace_bytes(const AttnPlan& p, int Hkv) {
 
 namespace {
 
-hipError_t launch_attn(const AttnPlan& plan, bool f8, const void* q, const void* k, const void* v,
+// Cache formats: bf16 values, FP8 codes with a row exponent, 4-bit codes with an exponent
+// per 32 values (always the 16-row or the 256-row kernel).
+enum CacheFmt { kBf16 = 0, kFp8 = 1, kMx4 = 2 };
+
+hipError_t launch_attn(const AttnPlan& plan, int fmt, const void* q, const void* k, const void* v,
                        const int32_t* ek, const int32_t* ev, int64_t st, int64_t sh, const int32_t* parent, int N,
                        int L, int Hq, int Hkv, float scale, void* out, float* lse, void* workspace,
                        int32_t* dev_error, hipStream_t stream) {
@@ -1570,21 +1701,34 @@ hipError_t launch_attn(const AttnPlan& plan, bool f8, const void* q, const void*
   sp.remap = (nwg % 8 == 0) ? 1 : 0;
 
   hipError_t e;
-  if (plan.M <= 16 && !f8) {
+  int merge_rows = plan.RWV * 32;  // stacked rows per split workgroup
+  if (plan.M <= 16 && fmt == kBf16) {
     static std::atomic<uint64_t> attr_devices{0};
     e = allow_dynamic_lds(&attn_rows16_kernel<false>, R16_SMEM_BYTES, attr_devices);
     if (e == hipSuccess) {
       hipLaunchKernelGGL(attn_rows16_kernel<false>, dim3(nwg), dim3(512), R16_SMEM_BYTES, stream, sp);
       e = hipGetLastError();
     }
-  } else if (plan.M <= 16) {
+  } else if (plan.M <= 16 && fmt == kFp8) {
     static std::atomic<uint64_t> attr_devices{0};
     e = allow_dynamic_lds(&attn_rows16_kernel<true>, R16_SMEM_BYTES, attr_devices);
     if (e == hipSuccess) {
       hipLaunchKernelGGL(attn_rows16_kernel<true>, dim3(nwg), dim3(512), R16_SMEM_BYTES, stream, sp);
       e = hipGetLastError();
     }
-  } else if (f8) {
+  } else if (plan.M <= 16) {
+    static std::atomic<uint64_t> attr_devices{0};
+    e = allow_dynamic_lds(&attn_rows16_kernel<true, true>, R16_SMEM_BYTES, attr_devices);
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL((attn_rows16_kernel<true, true>), dim3(nwg), dim3(512), R16_SMEM_BYTES, stream, sp);
+      e = hipGetLastError();
+    }
+  } else if (fmt == kMx4) {
+    // The 256-row kernel for any row count above 16: one row tile per KV head up to 256
+    // rows (RT, S and the workspace are those of the plan), idle row-waves past M.
+    e = launch_split<8, true, true>(sp, nwg, stream);
+    merge_rows = TILE_ROWS;
+  } else if (fmt == kFp8) {
     switch (plan.RWV) {
       case 1: e = launch_split<1, true>(sp, nwg, stream); break;
       case 2: e = launch_split<2, true>(sp, nwg, stream); break;
@@ -1611,7 +1755,7 @@ hipError_t launch_attn(const AttnPlan& plan, bool f8, const void* q, const void*
   mp.G = plan.G;
   mp.RT = plan.RT;
   mp.S = plan.S;
-  mp.rows = plan.RWV * 32;
+  mp.rows = merge_rows;
   const int rows_out = N * Hq;
   const dim3 mgrid((rows_out + 3) / 4);
   switch ((plan.S + 15) / 16) {
@@ -1629,7 +1773,7 @@ hipError_t launch_attn(const AttnPlan& plan, bool f8, const void* q, const void*
 hipError_t launch_tree_attn(const AttnPlan& plan, const void* q, const void* k, const void* v, int64_t st,
                             int64_t sh, const int32_t* parent, int N, int L, int Hq, int Hkv, float scale,
                             void* out, float* lse, void* workspace, int32_t* dev_error, hipStream_t stream) {
-  return launch_attn(plan, false, q, k, v, nullptr, nullptr, st, sh, parent, N, L, Hq, Hkv, scale, out, lse,
+  return launch_attn(plan, kBf16, q, k, v, nullptr, nullptr, st, sh, parent, N, L, Hq, Hkv, scale, out, lse,
                      workspace, dev_error, stream);
 }
 
@@ -1637,8 +1781,17 @@ hipError_t launch_tree_attn_fp8(const AttnPlan& plan, const void* q, const void*
                                 const int32_t* ek, const int32_t* ev, int64_t st, int64_t sh,
                                 const int32_t* parent, int N, int L, int Hq, int Hkv, float scale, void* out,
                                 float* lse, void* workspace, int32_t* dev_error, hipStream_t stream) {
-  return launch_attn(plan, true, q, kc, vc, ek, ev, st, sh, parent, N, L, Hq, Hkv, scale, out, lse, workspace,
+  return launch_attn(plan, kFp8, q, kc, vc, ek, ev, st, sh, parent, N, L, Hq, Hkv, scale, out, lse, workspace,
                      dev_error, stream);
+}
+
+hipError_t launch_tree_attn_mx4(const AttnPlan& plan, const void* q, const void* kc, const void* vc,
+                                const int8_t* ek, const int8_t* ev, int64_t st, int64_t sh,
+                                const int32_t* parent, int N, int L, int Hq, int Hkv, float scale, void* out,
+                                float* lse, void* workspace, int32_t* dev_error, hipStream_t stream) {
+  // a row's four int8 block exponents travel as one 32-bit word
+  return launch_attn(plan, kMx4, q, kc, vc, reinterpret_cast<const int32_t*>(ek), reinterpret_cast<const int32_t*>(ev),
+                     st, sh, parent, N, L, Hq, Hkv, scale, out, lse, workspace, dev_error, stream);
 }
 
 }  // namespace tv

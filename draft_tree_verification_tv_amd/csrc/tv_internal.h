@@ -212,6 +212,10 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const void* q, const void* k, 
                             int64_t st, int64_t sh, const int32_t* parent, int N, int L, int Hq,
                             int Hkv, float scale, void* out, float* lse, void* workspace,
                             int32_t* dev_error, hipStream_t stream);
+hipError_t launch_tree_attn_mx4(const AttnPlan& plan, const void* q, const void* kc, const void* vc,
+                                const int8_t* ek, const int8_t* ev, int64_t st, int64_t sh,
+                                const int32_t* parent, int N, int L, int Hq, int Hkv, float scale, void* out,
+                                float* lse, void* workspace, int32_t* dev_error, hipStream_t stream);
 hipError_t launch_tree_attn_fp8(const AttnPlan& plan, const void* q, const void* kc, const void* vc,
                                 const int32_t* ek, const int32_t* ev, int64_t st, int64_t sh,
                                 const int32_t* parent, int N, int L, int Hq, int Hkv, float scale, void* out,

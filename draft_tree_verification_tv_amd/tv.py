@@ -26,7 +26,8 @@ HEAD_DIM = 128
 EXPORTS = ("tv_abi_version", "tv_status_string", "tv_validate_tree_host", "tv_tree_prep",
            "tv_tree_attn_workspace_size", "tv_tree_attn", "tv_argmax_workspace_size",
            "tv_argmax", "tv_accept", "tv_argmax_accept", "tv_sample_accept", "tv_kv_commit",
-           "tv_kv_quantize_fp8", "tv_tree_attn_fp8", "tv_tree_attn_noalloc", "tv_kv_quantize_mx4")
+           "tv_kv_quantize_fp8", "tv_tree_attn_fp8", "tv_tree_attn_noalloc", "tv_kv_quantize_mx4",
+           "tv_tree_attn_mx4")
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
@@ -88,6 +89,9 @@ def lib():
                                        _i32, _vp, _vp, _vp, _sz, _vp, _vp]
         L.tv_kv_quantize_fp8.restype = _i32
         L.tv_kv_quantize_fp8.argtypes = [_vp, _i64, _i64, _i32, _i32, _i32, _vp, _i64, _i64, _vp, _vp]
+        L.tv_tree_attn_mx4.restype = _i32
+        L.tv_tree_attn_mx4.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i32, _i32, _i32, _i32, _i32,
+                                       _f32, _i32, _vp, _vp, _vp, _sz, _vp, _vp]
         L.tv_kv_quantize_mx4.restype = _i32
         L.tv_kv_quantize_mx4.argtypes = [_vp, _i64, _i64, _i32, _i32, _i32, _vp, _i64, _i64, _vp, _vp]
         if L.tv_abi_version() != 1:
@@ -321,6 +325,58 @@ def tree_attn_fp8(q, k_codes, v_codes, k_exps, v_exps, parent, L=None, scale=Non
                                   float(scale), int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace),
                                   _nbytes(workspace), _ptr(dev_error), _stream(stream)),
            "tv_tree_attn_fp8")
+    return out
+
+
+def tree_attn_mx4(q, k_codes, v_codes, k_exps, v_exps, parent, L=None, scale=None, num_splits=0, out=None,
+                  lse=None, workspace=None, dev_error=None, stream=None):
+    """Tree-masked attention over a 4-bit cache: k_codes, v_codes uint8 [>= L+N, Hkv, D / 2]
+    (two E2M1 codes per byte, last dim contiguous, shared strides); k_exps, v_exps int8
+    [>= L+N, Hkv, D / 32] contiguous (block scales 2^e, as kv_quantize_mx4 writes them).
+    Otherwise as tree_attn."""
+    _need_cuda("q", q, torch.bfloat16)
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [N, Hq, D] tensor")
+    N, Hq, D = q.shape
+    for name, t in (("k_codes", k_codes), ("v_codes", v_codes)):
+        _need_cuda(name, t, torch.uint8)
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be 3-D")
+    if k_codes.stride() != v_codes.stride() or k_codes.stride(2) != 1:
+        raise ValueError("k_codes and v_codes must share strides with a contiguous last dim")
+    Hkv = k_codes.shape[1]
+    if k_codes.shape[1:] != (Hkv, D // 2) or v_codes.shape[1:] != (Hkv, D // 2):
+        raise ValueError(f"k_codes and v_codes must be [rows, Hkv, {D // 2}] with one Hkv")
+    for name, t in (("k_exps", k_exps), ("v_exps", v_exps)):
+        _need_cuda(name, t, torch.int8)
+        if t.dim() != 3 or not t.is_contiguous() or t.shape[1:] != (Hkv, D // 32):
+            raise ValueError(f"{name} must be a contiguous [T, Hkv, {D // 32}] tensor")
+    dev = q.device
+    for t in (k_codes, v_codes, k_exps, v_exps):
+        if t.device != dev:
+            raise ValueError("q, the codes and the exponents must be on one device")
+    _need_buf("parent", parent, torch.int32, shape=(N,), device=dev)
+    if L is None:
+        L = k_codes.shape[0] - N
+    rows = L + N
+    if L < 0 or min(k_codes.shape[0], v_codes.shape[0], k_exps.shape[0], v_exps.shape[0]) < rows:
+        raise ValueError("codes and exponents must hold L + N rows")
+    _opt_buf("out", out, torch.bfloat16, shape=(N, Hq, D), device=dev)
+    _opt_buf("lse", lse, torch.float32, shape=(N, Hq), device=dev)
+    _opt_buf("dev_error", dev_error, torch.int32, min_numel=1, device=dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((N, Hq, D), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        ws_bytes = tree_attn_workspace_size(N, L, Hq, Hkv, D, num_splits)
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    _need_workspace("workspace", workspace, dev)
+    _check(lib().tv_tree_attn_mx4(_ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_exps), _ptr(v_exps),
+                                  k_codes.stride(0), k_codes.stride(1), _ptr(parent), N, L, Hq, Hkv, D,
+                                  float(scale), int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace),
+                                  _nbytes(workspace), _ptr(dev_error), _stream(stream)),
+           "tv_tree_attn_mx4")
     return out
 
 

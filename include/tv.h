@@ -22,6 +22,7 @@
  *   tv_kv_commit  moves the accepted nodes' K/V rows behind the context   (bit exact)
  *   tv_kv_quantize_fp8   bf16 cache -> FP8 (E4M3) codes + per-row scales      (bit exact)
  *   tv_kv_quantize_mx4   bf16 cache -> 4-bit (E2M1) codes + per-32 scales     (bit exact)
+ *   tv_tree_attn_mx4     tree attention over that 4-bit cache
  *   tv_tree_attn_fp8     tree attention over that FP8 cache
  *
  * Conventions shared by every call
@@ -162,6 +163,30 @@ int tv_tree_attn_noalloc(const void* q, const void* k, const void* v, int64_t kv
  */
 int tv_tree_attn_fp8(const void* q, const void* k_codes, const void* v_codes,
                      const int32_t* k_exps, const int32_t* v_exps, int64_t kv_stride_t,
+                     int64_t kv_stride_h, const int32_t* parent, int N, int L, int Hq,
+                     int Hkv, int D, float scale, int num_splits, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, int32_t* dev_error,
+                     void* stream);
+
+/*
+ * Tree attention over a 4-bit key/value cache (the sub-8-bit cache of Lucebox-Hub review,
+ * section "2. DFlash"; format of tv_kv_quantize_mx4). Computes tv_tree_attn on the
+ * dequantised cache k[t][h][d] = decode(code of d) * 2^k_exps[(t * Hkv + h) * 4 + d / 32]
+ * (and likewise v), which is exact in bf16: the result is the bf16 call's on those values.
+ *   k_codes, v_codes   uint8, two E2M1 codes per byte (value 2j in the low nibble of byte
+ *                      j); row (t, kvh) of D / 2 bytes at base + t*kv_stride_t +
+ *                      kvh*kv_stride_h (strides in bytes, multiples of 16; 16-byte aligned
+ *                      base).
+ *   k_exps, v_exps     int8 [>= L + N][Hkv][4], contiguous, 4-byte aligned; each in
+ *                      [-125, 125] (what tv_kv_quantize_mx4 writes). An exponent outside is
+ *                      clamped into the range and, when dev_error is non-NULL,
+ *                      TV_ERR_INVALID_ARG is stored there.
+ *   The other arguments, the workspace (tv_tree_attn_workspace_size) and the limits are
+ *   those of tv_tree_attn, with (L + N) * kv_stride_t and (L + N) * Hkv * 4 bytes below
+ *   4 GiB. Above 16 stacked rows per KV head the call always runs the 256-row kernel.
+ */
+int tv_tree_attn_mx4(const void* q, const void* k_codes, const void* v_codes,
+                     const int8_t* k_exps, const int8_t* v_exps, int64_t kv_stride_t,
                      int64_t kv_stride_h, const int32_t* parent, int N, int L, int Hq,
                      int Hkv, int D, float scale, int num_splits, void* out, float* lse,
                      void* workspace, size_t workspace_bytes, int32_t* dev_error,

@@ -13,6 +13,7 @@ from .kvquant import (  # noqa: F401
     e4m3_decode,
     e4m3_encode,
     mx4_block_exponent,
+    mx4_block_exponents,
     quantize_kv,
     quantize_kv_mx4,
     row_scale_exponent,

@@ -142,19 +142,20 @@ def e2m1_encode(y) -> np.ndarray:
     """Nearest E2M1 code (uint8 0 .. 15) of float64 values, ties to the even code,
     saturating at +-6; -0 and negative values rounding to zero give code 0.
 
-    Written as a search over the eight non-negative code values: the nearest wins, at an
-    exact midpoint the code with mantissa bit 0."""
+    The same search as e4m3_encode, over the eight non-negative code values: the nearest
+    value wins; at an exact midpoint the code with mantissa bit 0 wins."""
     y = np.asarray(y, dtype=np.float64)
     if np.any(~np.isfinite(y)):
         raise ValueError("values must be finite")
     codes = np.arange(8, dtype=np.uint8)
-    vals = e2m1_decode(codes)
+    vals = e2m1_decode(codes)                                 # ascending
     a = np.minimum(np.abs(y).ravel(), E2M1_MAX)
-    d = np.abs(vals[None, :] - a[:, None])                   # distance to every value
-    best = d.min(axis=1, keepdims=True)
-    tied = d == best
-    even = tied & ((codes[None, :] & 1) == 0)
-    pick = np.where(even.any(axis=1), even.argmax(axis=1), tied.argmax(axis=1)).astype(np.uint8)
+    idx = np.searchsorted(vals, a)                            # vals[idx-1] < a <= vals[idx]
+    hi = np.clip(idx, 0, 7)
+    lo = np.clip(idx - 1, 0, 7)
+    d_hi, d_lo = vals[hi] - a, a - vals[lo]
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((codes[hi] & 1) == 0))
+    pick = np.where(pick_hi, codes[hi], codes[lo]).astype(np.uint8)
     sign = (y.ravel() < 0) & (pick != 0)
     return (pick | np.where(sign, 0x8, 0).astype(np.uint8)).reshape(y.shape)
 
@@ -169,6 +170,14 @@ def mx4_block_exponent(amax: float) -> int:
     return min(max(e, MX4_EXP_MIN), MX4_EXP_MAX)
 
 
+def mx4_block_exponents(amax) -> np.ndarray:
+    """mx4_block_exponent over an array of block maxima (frexp is exact in float64)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    m, k = np.frexp(amax)
+    e = np.clip(np.where(m <= 0.75, k - 3, k - 2), MX4_EXP_MIN, MX4_EXP_MAX)
+    return np.where(amax == 0, 0, e).astype(np.int64)
+
+
 def quantize_kv_mx4(bits) -> tuple[np.ndarray, np.ndarray]:
     """bf16 bits [T, H, D] -> (packed E2M1 codes uint8 [T, H, D / 2], block exponents int8
     [T, H, D / 32]). Each block is scaled by 2^-e (exact) and encoded."""
@@ -176,7 +185,7 @@ def quantize_kv_mx4(bits) -> tuple[np.ndarray, np.ndarray]:
     T, H, D = bits.shape
     x = bf16_bits_to_f64(bits).reshape(T, H, D // MX4_BLOCK, MX4_BLOCK)
     amax = np.abs(x).max(axis=3)
-    exps = np.vectorize(mx4_block_exponent, otypes=[np.int64])(amax) if amax.size else np.zeros(amax.shape, np.int64)
+    exps = mx4_block_exponents(amax)
     codes = e2m1_encode(np.ldexp(x, -exps[..., None])).reshape(T, H, D)
     packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
     return packed, exps.astype(np.int8)

@@ -10,7 +10,7 @@ import torch
 
 import draft_tree_verification_tv_amd as tv
 import oracle
-from tests.gpu_util import dev_bf16, note
+from tests.gpu_util import check_attention, dev_bf16, note
 from workloads import bf16_bits_from_f32, make
 
 pytestmark = pytest.mark.gpu
@@ -140,5 +140,197 @@ def test_quantize_full_size_cache_sampled_rows():
         assert np.array_equal(c[-3:], rc) and np.array_equal(e[-3:], re_)
         # every exponent: block maxima of the whole cache, by the oracle's scalar rule
         amax = np.abs(oracle.bf16_bits_to_f64(arr).reshape(arr.shape[0], arr.shape[1], 4, 32)).max(axis=3)
-        ref_e = np.vectorize(oracle.mx4_block_exponent, otypes=[np.int64])(amax)
+        ref_e = oracle.mx4_block_exponents(amax)
         assert np.array_equal(e.astype(np.int64), ref_e)
+
+
+# ------------------------------------------------------------ 4-bit tree attention
+
+
+def _dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def _dev_i8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int8)).cuda()
+
+
+def _dev_i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def _mx4_attn_gpu(q_bits, kc, ke, vc, ve, parent, L, scale, num_splits=0, dev_error=None):
+    N, Hq, _ = q_bits.shape
+    lse = torch.empty((N, Hq), dtype=torch.float32, device="cuda")
+    out = tv.tree_attn_mx4(dev_bf16(q_bits), _dev_u8(kc), _dev_u8(vc), _dev_i8(ke), _dev_i8(ve),
+                           _dev_i32(parent), L=L, scale=scale, num_splits=num_splits, lse=lse, dev_error=dev_error)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _mx4_ref(q_bits, kc, ke, vc, ve, parent, scale):
+    return oracle.tree_attention(oracle.bf16_bits_to_f64(q_bits), oracle.dequantize_kv_mx4(kc, ke),
+                                 oracle.dequantize_kv_mx4(vc, ve), parent, scale)
+
+
+def _check_mx4_workload(w, label, num_splits=0):
+    kc, ke = oracle.quantize_kv_mx4(w.k)
+    vc, ve = oracle.quantize_kv_mx4(w.v)
+    note(f"mx4 attention {label}: L={w.L} N={w.N} Hq={w.Hq} Hkv={w.Hkv} splits={num_splits}")
+    out, lse = _mx4_attn_gpu(w.q, kc, ke, vc, ve, w.parent, w.L, w.scale, num_splits)
+    ref, lref = _mx4_ref(w.q, kc, ke, vc, ve, w.parent, w.scale)
+    return check_attention(out, ref, lse, lref, label)
+
+
+@pytest.mark.parametrize("name,trials", [("tiny_chain", 3), ("budget22", 3), ("branch_8k", 2)])
+def test_mx4_attention_small_workloads(name, trials):
+    for trial in range(trials):
+        _check_mx4_workload(make(name, trial), f"{name}/{trial}")
+
+
+MX4_EDGE = [
+    ("L0_N1", dict(L=0, N=1, tree="chain", Hq=8, Hkv=2)),
+    ("L1_N5", dict(L=1, N=5, tree="random16", Hq=4, Hkv=1)),
+    ("L63_N1", dict(L=63, N=1, tree="chain", Hq=2, Hkv=2)),
+    ("L65_N3_mha", dict(L=65, N=3, tree="random16", Hq=1, Hkv=1)),
+    ("L130_N2", dict(L=130, N=2, tree="chain", Hq=8, Hkv=8)),
+    ("L200_N60", dict(L=200, N=60, tree="random16", Hq=8, Hkv=2)),
+    ("L1000_kary256_G1", dict(L=1000, N=256, tree="kary4", Hq=8, Hkv=8)),
+    ("L300_kary256_G8", dict(L=300, N=256, tree="kary4", Hq=16, Hkv=2)),
+    ("L777_G6_chain16", dict(L=777, N=16, tree="chain", Hq=24, Hkv=4)),
+    ("L4097_N64", dict(L=4097, N=64, tree="random16", Hq=32, Hkv=8)),
+    ("N3_G8_24rows", dict(L=500, N=3, tree="random16", Hq=8, Hkv=1)),
+    ("N17_G1_17rows", dict(L=3000, N=17, tree="random16", Hq=4, Hkv=4)),
+]
+
+
+@pytest.mark.parametrize("label,ov", MX4_EDGE, ids=[e[0] for e in MX4_EDGE])
+def test_mx4_attention_edge_shapes(label, ov):
+    _check_mx4_workload(make("budget22", 7, **ov), label)
+
+
+MX4_ROWS16 = [
+    ("chain16_G1", dict(L=1000, N=16, tree="chain", Hq=8, Hkv=8)),
+    ("N4_G4", dict(L=2500, N=4, tree="random16", Hq=16, Hkv=4)),
+    ("N2_G8_L0", dict(L=0, N=2, tree="chain", Hq=8, Hkv=1)),
+    ("N11_G1_L31", dict(L=31, N=11, tree="random16", Hq=3, Hkv=3)),
+    ("N3_G5_L96", dict(L=96, N=3, tree="random16", Hq=10, Hkv=2)),
+    ("N1_G8_peaky", dict(L=20000, N=1, tree="chain", Hq=8, Hkv=1, peaky=True)),
+]
+
+
+@pytest.mark.parametrize("label,ov", MX4_ROWS16, ids=[e[0] for e in MX4_ROWS16])
+def test_mx4_attention_rows16(label, ov):
+    w = make("budget22", 13, **ov)
+    assert w.N * w.Hq // w.Hkv <= 16
+    _check_mx4_workload(w, f"16-row {label}")
+
+
+# T = 7022 keys, 110 tiles: 1, 2, 3, 7, 19, 37, 55 and 110 splits (both merge kernels),
+# 88 rows through the 256-row kernel.
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 20, 40, 55, 1024])
+def test_mx4_attention_forced_splits(splits):
+    _check_mx4_workload(make("budget22", 11, L=7000, N=22), f"splits={splits}", num_splits=splits)
+
+
+@pytest.mark.parametrize("splits", [1, 4, 40, 1024])
+def test_mx4_attention_decode_splits(splits):
+    _check_mx4_workload(make("decode_1node", 3, L=5000), f"decode splits={splits}", num_splits=splits)
+
+
+@pytest.mark.parametrize("L,splits", [(700, 12), (700, 6), (700, 4), (700, 3), (700, 2), (700, 1), (1200, 4)])
+def test_mx4_attention_dense_short_splits(L, splits):
+    _check_mx4_workload(make("branch_8k", 4, L=L), f"8x1 L={L} splits={splits}", num_splits=splits)
+
+
+def test_mx4_attention_peaky_keys():
+    _check_mx4_workload(make("max_256k", 1, L=20000), "peaky 20k")
+
+
+def test_mx4_attention_own_key_only_is_exact():
+    """Every node a root with L = 0: node i sees only its own key, so its output is its
+    dequantised V row exactly (p = 1); V blocks span exponents from -125 to 125."""
+    rng = np.random.default_rng(9)
+    N, Hq, Hkv = 256, 8, 4
+    parent = np.full(N, -1, np.int32)
+    q = bf16_bits_from_f32(rng.standard_normal((N, Hq, 128)).astype(np.float32))
+    k = bf16_bits_from_f32(rng.standard_normal((N, Hkv, 128)).astype(np.float32))
+    v32 = rng.standard_normal((N, Hkv, 4, 32)).astype(np.float32)
+    shifts = rng.integers(-110, 110, size=(N, Hkv, 4, 1))
+    shifts[0, 0, 0] = -122                    # block exponent at the low end
+    shifts[1, 0, 3] = 124                     # and at the high end
+    v64 = v32.astype(np.float64) / np.abs(v32).max(axis=3, keepdims=True) * np.exp2(shifts.astype(np.float64))
+    v = bf16_bits_from_f32(v64.reshape(N, Hkv, 128).astype(np.float32))
+    kc, ke = oracle.quantize_kv_mx4(k)
+    vc, ve = oracle.quantize_kv_mx4(v)
+    assert ve.min() <= -120 and ve.max() >= 120 and ve.min() >= -125 and ve.max() <= 125
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out, lse = _mx4_attn_gpu(q, kc, ke, vc, ve, parent, 0, 1 / np.sqrt(128), dev_error=err)
+    assert err.item() == 0
+    deq = oracle.dequantize_kv_mx4(vc, ve)
+    expect = np.repeat(deq, Hq // Hkv, axis=1)
+    got = out.float().cpu().numpy().astype(np.float64)
+    bad = np.argwhere(got != expect)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first {bad[0]}"
+    _, lref = _mx4_ref(q, kc, ke, vc, ve, parent, 1 / np.sqrt(128))
+    assert np.abs(lse.cpu().numpy() - lref).max() < 1e-3
+
+
+def test_mx4_attention_strided_cache():
+    """Codes as views into a larger cache (every other head of [T, 2*Hkv, D/2]) and
+    exponents sized for a longer cache than L + N."""
+    w = make("budget22", 3, L=1500)
+    kc, ke = oracle.quantize_kv_mx4(w.k)
+    vc, ve = oracle.quantize_kv_mx4(w.v)
+    T = w.L + w.N
+    big_k = np.zeros((T + 5, 2 * w.Hkv, 64), np.uint8)
+    big_v = np.zeros_like(big_k)
+    big_k[:T, ::2] = kc
+    big_v[:T, ::2] = vc
+    ke_big = np.zeros((T + 9, w.Hkv, 4), np.int8)
+    ve_big = np.zeros_like(ke_big)
+    ke_big[:T], ve_big[:T] = ke, ve
+    out = tv.tree_attn_mx4(dev_bf16(w.q), _dev_u8(big_k)[:, ::2], _dev_u8(big_v)[:, ::2], _dev_i8(ke_big),
+                           _dev_i8(ve_big), _dev_i32(w.parent), L=w.L, scale=w.scale)
+    ref, _ = _mx4_ref(w.q, kc, ke, vc, ve, w.parent, w.scale)
+    check_attention(out, ref, label="mx4 strided")
+
+
+# budget22 (88 rows) widens shared tiles; decode (8 rows) widens each wave's own blocks.
+@pytest.mark.parametrize("name", ["budget22", "decode_1node"])
+def test_mx4_attention_out_of_range_exponent_is_reported(name):
+    w = make(name, 2, L=200)
+    kc, ke = oracle.quantize_kv_mx4(w.k)
+    vc, ve = oracle.quantize_kv_mx4(w.v)
+    for bad_e in (126, -126, -128):
+        ve2 = ve.copy()
+        ve2[17, 0, 2] = bad_e
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        _mx4_attn_gpu(w.q, kc, ke, vc, ve2, w.parent, w.L, w.scale, dev_error=err)
+        assert err.item() == 1, bad_e
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    _mx4_attn_gpu(w.q, kc, ke, vc, ve, w.parent, w.L, w.scale, dev_error=err)
+    assert err.item() == 0
+
+
+def test_mx4_gpu_quantise_then_attend_full_size():
+    """long_128k: the cache quantised on the GPU (checked code for code against the
+    oracle's) feeds the 4-bit attention; reference: the oracle on the oracle's dequantised
+    cache."""
+    w = make("long_128k", 0, parts=("tree", "qkv"))
+    note("mx4 full size: gpu quantise")
+    kc_d, ke_d = tv.kv_quantize_mx4(dev_bf16(w.k))
+    vc_d, ve_d = tv.kv_quantize_mx4(dev_bf16(w.v))
+    lse = torch.empty((w.N, w.Hq), dtype=torch.float32, device="cuda")
+    out = tv.tree_attn_mx4(dev_bf16(w.q), kc_d, vc_d, ke_d, ve_d, _dev_i32(w.parent), L=w.L, scale=w.scale,
+                           lse=lse)
+    torch.cuda.synchronize()
+    note("mx4 full size: oracle quantise")
+    kc, ke = oracle.quantize_kv_mx4(w.k)
+    vc, ve = oracle.quantize_kv_mx4(w.v)
+    assert np.array_equal(kc_d.cpu().numpy(), kc) and np.array_equal(ke_d.cpu().numpy(), ke)
+    assert np.array_equal(vc_d.cpu().numpy(), vc) and np.array_equal(ve_d.cpu().numpy(), ve)
+    note("mx4 full size: oracle attention")
+    ref, lref = _mx4_ref(w.q, kc, ke, vc, ve, w.parent, w.scale)
+    e, r = check_attention(out, ref, lse, lref, "mx4 long_128k")
+    note(f"mx4 long_128k: max abs {e:.2e} row rel {r:.2e}")

@@ -154,3 +154,11 @@ def test_mutant_round_half_away_is_caught():
         return (idx | np.where(sign, 8, 0)).astype(np.uint8)
     assert not _midpoints_ok(encode_half_away)
     assert _midpoints_ok(oracle.e2m1_encode)
+
+
+def test_block_exponents_vectorised_equal_scalar():
+    rng = np.random.default_rng(7)
+    amax = np.exp2(rng.uniform(-140, 130, 20000)) * rng.uniform(0.5, 1.0, 20000)
+    amax = np.concatenate([amax, [0.0, 6.0, 3.0, 0.75, 0.7500001, 2.0 ** -140, 2.0 ** 127 * 1.99]])
+    want = np.array([oracle.mx4_block_exponent(float(a)) for a in amax])
+    assert np.array_equal(oracle.mx4_block_exponents(amax), want)
