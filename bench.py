@@ -338,6 +338,20 @@ def main():
     fp8_us = timed(fp8_call, reps=8 * nf8, warm=4 * nf8)
     del f8
 
+    # 4-bit cache: the same four layers quantised on the GPU, then the tree attention over
+    # them in turn.
+    mx = [(tv.kv_quantize_mx4(K[b]), tv.kv_quantize_mx4(Vc[b])) for b in range(nf8)]
+    mx_quant_us = timed(lambda: tv.kv_quantize_mx4(K[1], codes=mx[1][0][0], exps=mx[1][0][1]))
+    mx_turn = [0]
+
+    def mx4_call():
+        (kc, ke), (vc, ve) = mx[mx_turn[0] % nf8]
+        mx_turn[0] += 1
+        tv.tree_attn_mx4(q, kc, vc, ke, ve, parent, L=L, scale=w.scale, num_splits=args.splits, out=out,
+                         workspace=ws)
+    mx4_us = timed(mx4_call, reps=8 * nf8, warm=4 * nf8)
+    del mx
+
     # Streaming reference on this machine: a plain 1 GiB device-to-device copy (read and
     # write counted), the best of five; context for the roofline fraction.
     cp_n = 1 << 30
@@ -483,7 +497,8 @@ def main():
                          "attn_p90": round(float(np.percentile(attn_ms, 90) * 1e3), 2)},
         "graph_ms_per_step": round(graph_ms_per_step, 3),
         "next_rows_us": {"sample_accept_T1": round(sample_us, 2), "kv_commit": round(commit_us, 2),
-                         "tree_attn_fp8": round(fp8_us, 2), "kv_quantize_fp8_one_tensor": round(quant_us, 2)},
+                         "tree_attn_fp8": round(fp8_us, 2), "kv_quantize_fp8_one_tensor": round(quant_us, 2),
+                         "tree_attn_mx4": round(mx4_us, 2), "kv_quantize_mx4_one_tensor": round(mx_quant_us, 2)},
         "kv_gbps": round(kv_gbps, 1),
         "kv_hbm_frac": round(kv_gbps / HBM_PEAK_GBS, 4),
         "hbm_copy_gbps": round(copy_gbps, 1),
