@@ -193,7 +193,7 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
   constexpr int NW = RWV * KSW;
   constexpr int ROWS = RWV * 32;  // stacked rows per workgroup
   static_assert(NW == 8, "eight waves per workgroup");
-  static_assert(!kMX || (kF8 && RWV == 8), "the 4-bit cache runs the 256-row kernel");
+  static_assert(!kMX || (kF8 && RWV >= 2), "the 4-bit cache runs the shared-ring kernels");
   // Copies per wave per tile: bf16, 16 blocks of 1 KB for each of K and V; FP8, 8 blocks
   // of codes for each plus one copy of 128 / NW exponents; 4-bit, one of the 4 + 4 code
   // blocks plus one copy of 16 exponent words.
@@ -1724,10 +1724,15 @@ hipError_t launch_attn(const AttnPlan& plan, int fmt, const void* q, const void*
       e = hipGetLastError();
     }
   } else if (fmt == kMx4) {
-    // The 256-row kernel for any row count above 16: one row tile per KV head up to 256
-    // rows (RT, S and the workspace are those of the plan), idle row-waves past M.
-    e = launch_split<8, true, true>(sp, nwg, stream);
-    merge_rows = TILE_ROWS;
+    // The shared-ring kernels (two, four or eight row-waves); 17-32 rows take the two
+    // row-wave one (one row tile per KV head either way, so RT, S and the workspace are
+    // those of the plan).
+    switch (plan.RWV) {
+      case 1:
+      case 2: e = launch_split<2, true, true>(sp, nwg, stream); merge_rows = 64; break;
+      case 4: e = launch_split<4, true, true>(sp, nwg, stream); break;
+      default: e = launch_split<8, true, true>(sp, nwg, stream); break;
+    }
   } else if (fmt == kFp8) {
     switch (plan.RWV) {
       case 1: e = launch_split<1, true>(sp, nwg, stream); break;
