@@ -45,10 +45,10 @@ CPU_SAMPLE_SECONDS = 10.0
 # profiles/tv_tree_attn_long_128k_hbm_counters.md. Valid only for the kernel sources they
 # were taken on (compared through a digest of their code without comments): reported as
 # null once that code changes.
-TRAFFIC_BYTES_PER_CALL = 572942354
+TRAFFIC_BYTES_PER_CALL = 572951399
 TRAFFIC_SOURCES = ("draft_tree_verification_tv_amd/csrc/tv_attn.hip",
                    "draft_tree_verification_tv_amd/csrc/tv_internal.h")
-TRAFFIC_SOURCES_SHA256 = "bd4c964dfa6925933a7697a5e6636edbd6e7bc4751c9decdbe2485104f460f95"
+TRAFFIC_SOURCES_SHA256 = "6c9bbe6457379a1578fbb2129b958315064b8255ab862d0a7187b7f31086d323"
 
 
 def code_digest(root, files):
