@@ -134,7 +134,14 @@ __global__ __launch_bounds__(512) void coissue_kernel(const float* __restrict__ 
 
 // Every CU at once: `iters` iterations of eight v_mfma_f32_32x32x16_bf16 on four
 // independent accumulators. LSTEP 1: each MFMA's A operand is a fresh 16-byte LDS read per
-// lane (1 KB per wave); LSTEP 2: every second one is (0.5 KB per MFMA); 0: none. VALU: each
+// lane (1 KB per wave); LSTEP 2: every second one is (0.5 KB per MFMA); 0: none. LSTEP 3-5
+// read 1 KB per MFMA in the attention tiles' layout (64 rows of 256 bytes, the K and V
+// chunk swizzles, four 16 KB stages): 3, the attention loop's own mix, alternates a K
+// fragment (one 128-bit read per lane, rows = lane % 32) with a V^T fragment (two
+// ds_read_b64_tr_b16 per lane); 4 reads only V^T fragments, 5 only K fragments. LSTEP 6
+// and 7 model a wave of 64 rows, where each fragment feeds two MFMAs (one per 32-row
+// half): 6 reads K, -, V^T, - per four MFMAs (0.5 KB per MFMA); 7 reads K, K, V^T, - (the
+// second K read standing for a Q fragment kept in LDS, 0.75 KB per MFMA). VALU: each
 // MFMA is followed by one exp2 and four FMAs on independent values. Nothing depends on
 // anything else, so this is the most such a mix can reach. Wave 0 of workgroup 0 records
 // shader cycles and real-time ticks around its loop in clk[0], clk[1].
@@ -160,15 +167,38 @@ __global__ __launch_bounds__(512) void mix_kernel(const float* __restrict__ in, 
     r0 = __builtin_amdgcn_s_memrealtime();
     t0 = __builtin_amdgcn_s_memtime();
   }
+  // Attention-tile offsets: K row ql, chunk 2*s + grp; V^T rows 4*grp + i16/4 (and +8),
+  // head-dim columns db*32 + g16*16 + 4*(i16%4); both with their tiles' chunk swizzles.
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const int ql = lane & 31, grp = lane >> 5, i16 = lane & 15, g16 = (lane >> 4) & 1;
+  int koff[4], voff[4];
+  for (int s = 0; s < 4; ++s) koff[s] = ql * 256 + (((2 * s + grp) ^ (ql & 15)) << 4);
+  {
+    const int row = 4 * grp + (i16 >> 2), sw = (0xCA60 >> ((row & 3) * 4)) & 15;
+    for (int db = 0; db < 4; ++db)
+      voff[db] = row * 256 + (((db * 4 + g16 * 2 + ((i16 & 3) >> 1)) ^ sw) << 4) + (i16 & 1) * 8;
+  }
   f32x16 acc[4];
   for (int j = 0; j < 4; ++j) acc[j] = f32x16{};
   for (int it = 0; it < iters; ++it) {
+    const char* stage = lds + (it & 3) * 16384 + ((it >> 2) & 1) * 8192;  // + < 8 KB of rows
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       bf16x8 aa = a;
-      if (LSTEP > 0 && m % LSTEP == 0) {
+      const bool kread = LSTEP == 5 || (LSTEP == 3 && m % 2 == 0) || (LSTEP == 6 && m % 4 == 0) ||
+                         (LSTEP == 7 && m % 4 < 2);
+      const bool vread = LSTEP == 4 || (LSTEP == 3 && m % 2 == 1) || ((LSTEP == 6 || LSTEP == 7) && m % 4 == 2);
+      if ((LSTEP == 1 || LSTEP == 2) && m % LSTEP == 0) {
         const int off = ((it * 8 + m) * 1024 + lane * 16 + wave * 64) & (65536 - 16);
         aa = *reinterpret_cast<const bf16x8*>(lds + off);
+      } else if (kread) {
+        aa = *reinterpret_cast<const bf16x8*>(stage + koff[(m >> 1) & 3]);
+      } else if (vread) {
+        const char* a0 = stage + voff[(m >> 1) & 3];
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * 256));
+        aa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
       acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa, b, acc[m & 3], 0, 0, 0);
       if (VALU) {
@@ -235,19 +265,17 @@ int tv_probe_clock(uint64_t* out, uint64_t ticks, void* stream) {
 int tv_probe_mix(int lds_step, int valu, int threads, int workgroups, int iters, const float* in, float* out,
                  uint64_t* clk, void* stream) {
   if (!in || !out || !clk || iters < 1 || workgroups < 1 || workgroups > 65536 || (threads != 256 && threads != 512) ||
-      lds_step < 0 || lds_step > 2 || (valu != 0 && valu != 1))
+      lds_step < 0 || lds_step > 7 || (valu != 0 && valu != 1))
     return 1;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 g(workgroups), b(threads);
-  if (valu) {
-    if (lds_step == 0) hipLaunchKernelGGL((mix_kernel<0, true>), g, b, 0, st, in, out, clk, iters);
-    if (lds_step == 1) hipLaunchKernelGGL((mix_kernel<1, true>), g, b, 0, st, in, out, clk, iters);
-    if (lds_step == 2) hipLaunchKernelGGL((mix_kernel<2, true>), g, b, 0, st, in, out, clk, iters);
-  } else {
-    if (lds_step == 0) hipLaunchKernelGGL((mix_kernel<0, false>), g, b, 0, st, in, out, clk, iters);
-    if (lds_step == 1) hipLaunchKernelGGL((mix_kernel<1, false>), g, b, 0, st, in, out, clk, iters);
-    if (lds_step == 2) hipLaunchKernelGGL((mix_kernel<2, false>), g, b, 0, st, in, out, clk, iters);
-  }
+  typedef void (*mix_fn)(const float*, float*, uint64_t*, int);
+  static const mix_fn fns[2][8] = {
+      {mix_kernel<0, false>, mix_kernel<1, false>, mix_kernel<2, false>, mix_kernel<3, false>,
+       mix_kernel<4, false>, mix_kernel<5, false>, mix_kernel<6, false>, mix_kernel<7, false>},
+      {mix_kernel<0, true>, mix_kernel<1, true>, mix_kernel<2, true>, mix_kernel<3, true>, mix_kernel<4, true>,
+       mix_kernel<5, true>, mix_kernel<6, true>, mix_kernel<7, true>}};
+  hipLaunchKernelGGL(fns[valu][lds_step], g, b, 0, st, in, out, clk, iters);
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 

@@ -104,7 +104,10 @@ def coissue(mode: int, threads: int, iters: int = 2000):
 
 
 MIX_CASES = ((0, 0, "MFMA only"), (1, 0, "MFMA + 1 KB LDS reads each"), (0, 1, "MFMA + exp2 + 4 FMA each"),
-             (1, 1, "MFMA + 1 KB LDS + exp2 + 4 FMA each"), (2, 1, "MFMA + 0.5 KB LDS + exp2 + 4 FMA each"))
+             (1, 1, "MFMA + 1 KB LDS + exp2 + 4 FMA each"), (2, 1, "MFMA + 0.5 KB LDS + exp2 + 4 FMA each"),
+             (5, 0, "MFMA + K fragment (swizzled 128-bit)"), (4, 0, "MFMA + V^T fragment (2 transposed reads)"),
+             (3, 0, "MFMA + K / V^T fragments alternating"), (3, 1, "MFMA + K / V^T + exp2 + 4 FMA each"),
+             (6, 1, "64-row wave: K,-,V^T,- + exp2 + 4 FMA each"), (7, 1, "64-row wave: K,K,V^T,- + exp2 + 4 FMA"))
 
 
 def mix(lds_step: int, valu: int, threads: int, iters: int = 20000):

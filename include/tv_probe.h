@@ -60,7 +60,12 @@ int tv_probe_coissue(int mode, int threads, int iters, const float* in, float* o
  * `workgroups` workgroups of `threads` (256 or 512: one or two waves per SIMD) threads
  * each run `iters` iterations of eight v_mfma_f32_32x32x16_bf16 on four independent
  * accumulators. lds_step 1: every MFMA's A operand is a fresh 16-byte-per-lane LDS read
- * (1 KB per wave and MFMA); 2: every second MFMA's (0.5 KB); 0: no LDS reads. valu 1: each
+ * (1 KB per wave and MFMA); 2: every second MFMA's (0.5 KB); 0: no LDS reads. 3-5 read
+ * 1 KB per MFMA in the attention tiles' layout (256-byte rows, the K and V swizzles): 3
+ * alternates K fragments (128-bit reads) with V^T fragments (two ds_read_b64_tr_b16 per
+ * lane), the attention loop's mix; 4 reads only V^T fragments, 5 only K; 6 and 7 model 64
+ * rows per wave (each fragment feeding two MFMAs): 6 reads K, -, V^T, - per four MFMAs
+ * (0.5 KB per MFMA), 7 reads K, K, V^T, - (0.75 KB). valu 1: each
  * MFMA is followed by one exp2 and four FMAs on independent values; 0: none. Workgroup 0's
  * first wave writes clk[0] = shader-clock cycles and clk[1] = real-time ticks around its
  * loop (uint64 [2]). `in` (fp32, >= 1024 values) seeds the operands; `out` (fp32

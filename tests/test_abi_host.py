@@ -328,7 +328,8 @@ def test_probe_library_exports_and_validation():
     assert L.tv_probe_coissue(0, 64, 0, FAKE, FAKE, FAKE, None) == 1     # no iterations
     assert L.tv_probe_coissue(6, 64, 10, FAKE, FAKE, FAKE, None) == 1    # no such mode
     assert L.tv_probe_mix(0, 0, 512, 256, 10, None, FAKE, FAKE, None) == 1   # null input
-    assert L.tv_probe_mix(3, 0, 512, 256, 10, FAKE, FAKE, FAKE, None) == 1   # no such LDS step
+    assert L.tv_probe_mix(8, 0, 512, 256, 10, FAKE, FAKE, FAKE, None) == 1   # no such LDS step
+    assert L.tv_probe_mix(-1, 0, 512, 256, 10, FAKE, FAKE, FAKE, None) == 1  # no such LDS step
     assert L.tv_probe_mix(0, 2, 512, 256, 10, FAKE, FAKE, FAKE, None) == 1   # valu not 0 or 1
     assert L.tv_probe_mix(0, 0, 64, 256, 10, FAKE, FAKE, FAKE, None) == 1    # not 256 or 512 threads
     assert L.tv_probe_mix(0, 0, 512, 0, 10, FAKE, FAKE, FAKE, None) == 1     # no workgroups
