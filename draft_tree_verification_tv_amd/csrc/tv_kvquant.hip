@@ -27,40 +27,64 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float y0, float y1, float y2, flo
   return w & (nz | 0x7F7F7F7Fu);
 }
 
+// Rows per 16-lane group in both quantisers: all of a group's loads are issued before any
+// row is converted, so each lane keeps that many 16-byte loads in flight.
+constexpr int kQuantRows = 4;
+
+// Row (token, head) index -> its element offset in the source and byte offset in the codes;
+// rows < 2^31 (the host checks).
+struct RowAt {
+  int64_t src, codes;
+};
+__device__ __forceinline__ RowAt row_at(uint32_t row, int H, int64_t st, int64_t sh, int64_t cst, int64_t csh) {
+  const uint32_t t = row / (uint32_t)H, h = row - t * (uint32_t)H;
+  return {(int64_t)t * st + (int64_t)h * sh, (int64_t)t * cst + (int64_t)h * csh};
+}
+
 // 16 lanes per (token, head) row of 128 values, 8 per lane (one 16-byte load, one 8-byte
-// store); 16 rows per 256-thread block.
+// store); kQuantRows rows per group, 16 * kQuantRows rows per 256-thread block (row
+// 16 r + g of the block in group g, so that each load instruction covers consecutive rows).
 __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __restrict__ src, int64_t st, int64_t sh,
                                                           int T, int H, uint8_t* __restrict__ codes, int64_t cst,
                                                           int64_t csh, int32_t* __restrict__ exps) {
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const uint32_t rows = (uint32_t)T * (uint32_t)H;
+  const uint32_t row0 = blockIdx.x * (16u * kQuantRows) + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
-  if (row >= (int64_t)T * H) return;  // whole 16-lane groups leave together
-  const int64_t t = row / H;
-  const int h = (int)(row % H);
-  const u32x4 w = *reinterpret_cast<const u32x4*>(src + t * st + (int64_t)h * sh + 8 * sub);
-  float x[8];
+  u32x4 w[kQuantRows];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    x[2 * j] = bf16_lo(w[j]);
-    x[2 * j + 1] = bf16_hi(w[j]);
+  for (int r = 0; r < kQuantRows; ++r) {
+    const uint32_t row = row0 + 16u * r;
+    w[r] = u32x4{0u, 0u, 0u, 0u};
+    if (row < rows) w[r] = *reinterpret_cast<const u32x4*>(src + row_at(row, H, st, sh, 0, 0).src + 8 * sub);
   }
-  float amax = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
-  for (int off = 8; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  int e = 0;
-  if (amax > 0.f) {
-    int k;
-    const float m = frexpf(amax, &k);  // amax = m * 2^k, m in [0.5, 1); 448 = 0.875 * 2^9
-    e = m <= 0.875f ? k - 9 : k - 8;
+  for (int r = 0; r < kQuantRows; ++r) {
+    const uint32_t row = row0 + 16u * r;
+    if (row >= rows) break;  // whole 16-lane groups leave together
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = bf16_lo(w[r][j]);
+      x[2 * j + 1] = bf16_hi(w[r][j]);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+    for (int off = 8; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    int e = 0;
+    if (amax > 0.f) {
+      int k;
+      const float m = frexpf(amax, &k);  // amax = m * 2^k, m in [0.5, 1); 448 = 0.875 * 2^9
+      e = m <= 0.875f ? k - 9 : k - 8;
+    }
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = ldexpf(x[j], -e);  // exact: a power-of-two scaling
+    const uint32_t lo = e4m3_pack4(y[0], y[1], y[2], y[3]);
+    const uint32_t hi = e4m3_pack4(y[4], y[5], y[6], y[7]);
+    *reinterpret_cast<uint2*>(codes + row_at(row, H, 0, 0, cst, csh).codes + 8 * sub) = make_uint2(lo, hi);
+    if (sub == 0) exps[row] = e;
   }
-  float y[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) y[j] = ldexpf(x[j], -e);  // exact: a power-of-two scaling
-  const uint32_t lo = e4m3_pack4(y[0], y[1], y[2], y[3]);
-  const uint32_t hi = e4m3_pack4(y[4], y[5], y[6], y[7]);
-  *reinterpret_cast<uint2*>(codes + t * cst + (int64_t)h * csh + 8 * sub) = make_uint2(lo, hi);
-  if (sub == 0) exps[row] = e;
 }
 
 // ---- 4-bit cache: OCP FP4 (E2M1) elements, blocks of 32 values sharing one power-of-two
@@ -70,58 +94,63 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __rest
 // round x * 2^-e (exact) to the nearest E2M1 value, ties to the even code, saturating at 6
 // (reached only where e was clamped); a negative value that rounds to zero is coded +0.
 // Element 2j of a row is the low nibble of byte j.
+constexpr int kMxExpLo = -125, kMxExpHi = 125;
 
-// E2M1 code of y: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (codes 0 .. 7); each comparison
-// puts an exact midpoint on the side of the even code.
-__device__ __forceinline__ uint32_t e2m1_code(float y) {
-  const float a = fabsf(y);
-  const uint32_t c = a <= 0.25f ? 0u
-                     : a < 0.75f ? 1u
-                     : a <= 1.25f ? 2u
-                     : a < 1.75f ? 3u
-                     : a <= 2.5f ? 4u
-                     : a < 3.5f ? 5u
-                     : a <= 5.0f ? 6u
-                                 : 7u;
-  return (y < 0.f && c != 0u) ? (c | 8u) : c;
+// Eight E2M1 codes of a lane's eight bf16 values (four words of value pairs) with the
+// block scale 2^e: the hardware conversion divides each value by the scale (exact, a
+// power of two) and rounds to the nearest E2M1 value, ties to the even code, saturating
+// at 6; pair j goes to byte j, its first value to the low nibble. A negative value that
+// rounds to zero comes out as code 8 (-0) and is recoded +0: bit 0 of each nibble of
+// t = w | w >> 1 | w >> 2 is the OR of that nibble's three magnitude bits.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// A word as two bf16 values. The word comes in by value: bit-casting a vector element in
+// place (w[j] of an ext_vector) yields element 0 whatever j is, with this compiler.
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t x) { return __builtin_bit_cast(bf16x2_t, x); }
+
+__device__ __forceinline__ uint32_t e2m1_pack8(const u32x4& w, float scale) {
+  uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, as_bf16x2(w[0]), scale, 0);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, as_bf16x2(w[1]), scale, 1);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, as_bf16x2(w[2]), scale, 2);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, as_bf16x2(w[3]), scale, 3);
+  const uint32_t zero = ~(c | (c >> 1) | (c >> 2)) & 0x11111111u;
+  return c & ~(zero << 3);
 }
 
-// One thread per 32-value block: 4 threads per (token, head) row of 128 values, 64 rows
-// per 256-thread workgroup. Reads 64 bytes, writes 16 bytes of codes and one exponent.
+// The FP8 quantiser's layout: 16 lanes per (token, head) row of 128 values, 8 per lane
+// (one 16-byte load, one 4-byte store), so four lanes hold a 32-value block and exchange
+// their maxima; kQuantRows rows per group as there.
 __global__ __launch_bounds__(256) void kv_quantize_mx4_kernel(const uint16_t* __restrict__ src, int64_t st,
                                                               int64_t sh, int T, int H, uint8_t* __restrict__ codes,
                                                               int64_t cst, int64_t csh, int8_t* __restrict__ exps) {
-  const int64_t row = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
-  const int blk = threadIdx.x & 3;
-  if (row >= (int64_t)T * H) return;
-  const int64_t t = row / H;
-  const int h = (int)(row % H);
-  const uint16_t* xs = src + t * st + (int64_t)h * sh + 32 * blk;
-  float x[32];
+  const uint32_t rows = (uint32_t)T * (uint32_t)H;
+  const uint32_t row0 = blockIdx.x * (16u * kQuantRows) + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  u32x4 w[kQuantRows];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(xs + 8 * q);
+  for (int r = 0; r < kQuantRows; ++r) {
+    const uint32_t row = row0 + 16u * r;
+    w[r] = u32x4{0u, 0u, 0u, 0u};
+    if (row < rows) w[r] = *reinterpret_cast<const u32x4*>(src + row_at(row, H, st, sh, 0, 0).src + 8 * sub);
+  }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[8 * q + 2 * j] = bf16_lo(w[j]);
-      x[8 * q + 2 * j + 1] = bf16_hi(w[j]);
+  for (int r = 0; r < kQuantRows; ++r) {
+    const uint32_t row = row0 + 16u * r;
+    if (row >= rows) break;  // whole 16-lane groups leave together
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[r][j])), fabsf(bf16_hi(w[r][j]))));
+    for (int off = 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    int e = 0;
+    if (amax > 0.f) {
+      int k;
+      const float m = frexpf(amax, &k);  // amax = m * 2^k, m in [0.5, 1); 6 = 0.75 * 2^3
+      e = m <= 0.75f ? k - 3 : k - 2;
+      e = min(max(e, kMxExpLo), kMxExpHi);
     }
+    const uint32_t c = e2m1_pack8(w[r], __int_as_float((e + 127) << 23));
+    *reinterpret_cast<uint32_t*>(codes + row_at(row, H, 0, 0, cst, csh).codes + 4 * sub) = c;
+    if ((sub & 3) == 0) exps[(int64_t)row * 4 + (sub >> 2)] = (int8_t)e;
   }
-  float amax = 0.f;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(x[j]));
-  int e = 0;
-  if (amax > 0.f) {
-    int k;
-    const float m = frexpf(amax, &k);  // amax = m * 2^k, m in [0.5, 1); 6 = 0.75 * 2^3
-    e = m <= 0.75f ? k - 3 : k - 2;
-    e = min(max(e, -125), 125);
-  }
-  u32x4 out = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int j = 0; j < 32; ++j) out[j >> 3] |= e2m1_code(ldexpf(x[j], -e)) << (4 * (j & 7));
-  *reinterpret_cast<u32x4*>(codes + t * cst + (int64_t)h * csh + 16 * blk) = out;
-  exps[row * 4 + blk] = (int8_t)e;
 }
 
 }  // namespace
@@ -129,7 +158,8 @@ __global__ __launch_bounds__(256) void kv_quantize_mx4_kernel(const uint16_t* __
 hipError_t launch_kv_quantize_mx4(const void* src, int64_t st, int64_t sh, int T, int H, void* codes, int64_t cst,
                                   int64_t csh, int8_t* exps, hipStream_t stream) {
   const int64_t rows = (int64_t)T * H;
-  hipLaunchKernelGGL(kv_quantize_mx4_kernel, dim3((unsigned)((rows + 63) / 64)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(kv_quantize_mx4_kernel, dim3((unsigned)((rows + 16 * kQuantRows - 1) / (16 * kQuantRows))),
+                     dim3(256), 0, stream,
                      static_cast<const uint16_t*>(src), st, sh, T, H, static_cast<uint8_t*>(codes), cst, csh, exps);
   return hipGetLastError();
 }
@@ -137,7 +167,8 @@ hipError_t launch_kv_quantize_mx4(const void* src, int64_t st, int64_t sh, int T
 hipError_t launch_kv_quantize(const void* src, int64_t st, int64_t sh, int T, int H, void* codes, int64_t cst,
                               int64_t csh, int32_t* exps, hipStream_t stream) {
   const int64_t rows = (int64_t)T * H;
-  hipLaunchKernelGGL(kv_quantize_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(kv_quantize_kernel, dim3((unsigned)((rows + 16 * kQuantRows - 1) / (16 * kQuantRows))),
+                     dim3(256), 0, stream,
                      static_cast<const uint16_t*>(src), st, sh, T, H, static_cast<uint8_t*>(codes), cst, csh, exps);
   return hipGetLastError();
 }
