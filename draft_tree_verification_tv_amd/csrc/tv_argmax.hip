@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kBlock) void sample_partial(const char* __restrict_
 }
 
 // One workgroup finishes the verify step: thread i takes node row i's largest slice key
-// (loads batched 16 slices at a time, all unconditional, indices clamped: a repeated key
+// (loads batched 32 slices at a time, all unconditional, indices clamped: a repeated key
 // cannot change the maximum), keeps the token in LDS and runs the acceptance walk on the
 // tokens (the walk of tv_accept). The draft and parent entries and the first batch of keys
 // are loaded together, ahead of the tree preprocessing, so that their round trips overlap.
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(kBlock) void argmax_accept_kernel(
     int N, int chunks, const uint64_t* __restrict__ part, int32_t* tok, const int32_t* __restrict__ parent,
     const int32_t* __restrict__ draft, int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes,
     int32_t* __restrict__ accept_tokens, int32_t* __restrict__ bonus, int32_t* dev_error) {
-  constexpr int kBatch = 16;
+  constexpr int kBatch = 32;  // a bf16 row of up to 262144 values in one round trip
   __shared__ uint64_t anc[kMaxNodes * kAncWords];
   __shared__ int par[kMaxNodes];
   __shared__ int jmp[kMaxNodes];
