@@ -1633,11 +1633,14 @@ AttnPlan attn_plan(int N, int L, int Hq, int Hkv, int num_splits, int num_cus) {
   p.RWV = rows <= 32 ? 1 : rows <= 64 ? 2 : rows <= 128 ? 4 : 8;
   p.RT = (p.M + p.RWV * 32 - 1) / (p.RWV * 32);
   p.T = L + N;
-  const int tiles = (p.T + KT - 1) / KT;
+  // Split lengths are whole 64-key tiles for the shared-ring kernels; the 16-row kernel
+  // streams 32-key blocks, so its splits need only be whole blocks.
+  const int gran = p.M <= 16 ? 32 : KT;
+  const int tiles = (p.T + gran - 1) / gran;
   int S = num_splits;
   if (S <= 0) {
     // One workgroup per CU (the four LDS stages and the tree masks take 138 KB): enough
-    // splits to give every CU a workgroup, down to one 64-key tile per split. Short
+    // splits to give every CU a workgroup, down to one tile (block) per split. Short
     // sequences are latency-bound, so filling the chip beats saving partial-output
     // traffic; long ones get long splits anyway.
     const int units = Hkv * p.RT;
@@ -1646,7 +1649,7 @@ AttnPlan attn_plan(int N, int L, int Hq, int Hkv, int num_splits, int num_cus) {
   if (S > tiles) S = tiles;
   if (S < 1) S = 1;
   const int tps = (tiles + S - 1) / S;
-  p.KS = tps * KT;
+  p.KS = tps * gran;
   p.S = (p.T + p.KS - 1) / p.KS;
   return p;
 }

@@ -213,7 +213,7 @@ def test_fp8_attention_forced_splits(splits):
 
 
 # Eight stacked rows (the 16-row kernel): each wave streams and widens its own blocks.
-# T = 5001 keys: the requests give 1, 4, 40 and 79 splits of 158, 40, 4 and 2 blocks, so
+# T = 5001 keys: the requests give 1, 4, 40 and 157 splits of 157, 40, 4 and 1 blocks, so
 # with few blocks most waves have none, and the last block is cut by the end of the keys.
 @pytest.mark.parametrize("splits", [1, 4, 40, 1024])
 def test_fp8_attention_single_row_wave_splits(splits):

@@ -254,10 +254,10 @@ def test_attention_forced_splits(splits):
     check_attention(out, ref, lse, lref, f"splits={splits}")
 
 
-# One row-wave (N * G <= 32): every wave streams its own 32-key blocks. T = 5001 keys, 79
-# tiles: the requests give 1, 4, 40 and 79 splits of 158, 40, 4 and 2 blocks (the last
-# split's final block is cut by the end of the keys), so with 4 or 2 blocks most waves
-# have none.
+# At most 16 stacked rows: every wave streams its own 32-key blocks, and splits are whole
+# blocks. T = 5001 keys, 157 blocks: the requests give 1, 4, 40 and 157 splits of 157, 40,
+# 4 and 1 blocks (the last split's final block is cut by the end of the keys), so with 4
+# or 1 blocks most waves have none.
 @pytest.mark.parametrize("splits", [1, 4, 40, 1024])
 def test_attention_single_row_wave_splits(splits):
     w = make("decode_1node", 3, L=5000)
