@@ -45,10 +45,10 @@ CPU_SAMPLE_SECONDS = 10.0
 # profiles/tv_tree_attn_long_128k_hbm_counters.md. Valid only for the kernel sources they
 # were taken on (compared through a digest of their code without comments): reported as
 # null once that code changes.
-TRAFFIC_BYTES_PER_CALL = 572951399
+TRAFFIC_BYTES_PER_CALL = 572948442
 TRAFFIC_SOURCES = ("draft_tree_verification_tv_amd/csrc/tv_attn.hip",
                    "draft_tree_verification_tv_amd/csrc/tv_internal.h")
-TRAFFIC_SOURCES_SHA256 = "6c9bbe6457379a1578fbb2129b958315064b8255ab862d0a7187b7f31086d323"
+TRAFFIC_SOURCES_SHA256 = "6f28b838ad2918a1cfab386065851fe34eb4f2a180c6492e4c6d789037ec2981"
 
 
 def code_digest(root, files):
