@@ -334,3 +334,31 @@ def test_mx4_gpu_quantise_then_attend_full_size():
     ref, lref = _mx4_ref(w.q, kc, ke, vc, ve, w.parent, w.scale)
     e, r = check_attention(out, ref, lse, lref, "mx4 long_128k")
     note(f"mx4 long_128k: max abs {e:.2e} row rel {r:.2e}")
+
+
+@pytest.mark.parametrize("name", ["max_256k", "wide_tree", "decode_1node"])
+def test_mx4_full_size_sampled_heads(name):
+    """The other full-size workloads (the 4x2 kernel over 262160 keys, 2048 stacked rows in
+    eight row tiles, the 16-row kernel over 32769 keys): the whole cache quantised and
+    attended on the GPU; for the first and the last KV head the GPU's codes are checked
+    against the oracle's quantisation of that head, and the attention of that head's query
+    group against the oracle on the oracle's dequantised head."""
+    w = make(name, 0, parts=("tree", "qkv"))
+    G = w.Hq // w.Hkv
+    note(f"mx4 {name} full size: gpu quantise and attend")
+    kc_d, ke_d = tv.kv_quantize_mx4(dev_bf16(w.k))
+    vc_d, ve_d = tv.kv_quantize_mx4(dev_bf16(w.v))
+    lse = torch.empty((w.N, w.Hq), dtype=torch.float32, device="cuda")
+    out = tv.tree_attn_mx4(dev_bf16(w.q), kc_d, vc_d, ke_d, ve_d, _dev_i32(w.parent), L=w.L, scale=w.scale,
+                           lse=lse)
+    torch.cuda.synchronize()
+    for h in (0, w.Hkv - 1):
+        note(f"mx4 {name}: oracle, KV head {h}")
+        kc, ke = oracle.quantize_kv_mx4(w.k[:, h:h + 1])
+        vc, ve = oracle.quantize_kv_mx4(w.v[:, h:h + 1])
+        assert np.array_equal(kc_d[:, h:h + 1].cpu().numpy(), kc) and np.array_equal(ke_d[:, h:h + 1].cpu().numpy(), ke)
+        assert np.array_equal(vc_d[:, h:h + 1].cpu().numpy(), vc) and np.array_equal(ve_d[:, h:h + 1].cpu().numpy(), ve)
+        ref, lref = _mx4_ref(w.q[:, h * G:(h + 1) * G], kc, ke, vc, ve, w.parent, w.scale)
+        e, r = check_attention(out[:, h * G:(h + 1) * G], ref, lse[:, h * G:(h + 1) * G], lref,
+                               f"mx4 {name} head {h}")
+        note(f"mx4 {name} head {h}: max abs {e:.2e} row rel {r:.2e}")
