@@ -1633,7 +1633,7 @@ AttnPlan attn_plan(int N, int L, int Hq, int Hkv, int num_splits, int num_cus) {
   p.RWV = rows <= 32 ? 1 : rows <= 64 ? 2 : rows <= 128 ? 4 : 8;
   p.RT = (p.M + p.RWV * 32 - 1) / (p.RWV * 32);
   p.T = L + N;
-  // Split lengths are whole 64-key tiles for the shared-ring kernels; the 16-row kernel
+  // Split lengths are whole 64-key tiles for attn_split_kernel; the 16-row kernel
   // streams 32-key blocks, so its splits need only be whole blocks.
   const int gran = p.M <= 16 ? 32 : KT;
   const int tiles = (p.T + gran - 1) / gran;
