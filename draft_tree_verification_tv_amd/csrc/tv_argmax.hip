@@ -22,6 +22,7 @@
 #include <climits>
 #include <cmath>
 
+#include "tv_accept_wave.h"
 #include "tv_internal.h"
 
 namespace tv {
@@ -374,6 +375,49 @@ __global__ __launch_bounds__(kBlock) void argmax_accept_kernel(
   accept_block<kBlock>(anc, par, tok_s, draft_i, N, okw, red, accept_len, accept_nodes, accept_tokens, bonus);
 }
 
+// The same for at most 64 nodes: one wave (lane i = node row i), no LDS and no barrier.
+__global__ __launch_bounds__(64) void argmax_accept_wave_kernel(
+    int N, int chunks, const uint64_t* __restrict__ part, int32_t* tok, const int32_t* __restrict__ parent,
+    const int32_t* __restrict__ draft, int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes,
+    int32_t* __restrict__ accept_tokens, int32_t* __restrict__ bonus, int32_t* dev_error) {
+  constexpr int kBatch = 32;
+  const int i = threadIdx.x;
+  const bool valid = i < N;
+  const int draft_i = valid ? draft[i] : 0;
+  const int parent_i = valid ? parent[i] : -1;
+  int t = 0;
+  if (valid) {
+    if (chunks > 1) {
+      const uint64_t* pk = part + (int64_t)i * chunks;
+      uint64_t best = 0;
+      for (int j0 = 0; j0 < chunks; j0 += kBatch) {
+        uint64_t k[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) k[u] = pk[min(j0 + u, chunks - 1)];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) best = k[u] > best ? k[u] : best;
+      }
+      t = key_token(best);
+      tok[i] = t;
+    } else {
+      t = tok[i];
+    }
+  }
+  accept_wave(parent_i, draft_i, t, N, accept_len, accept_nodes, accept_tokens, bonus, dev_error);
+}
+
+// Argmax + accept finish: one wave for trees of at most 64 nodes, else one workgroup.
+void launch_finish(int N, int chunks, const uint64_t* part, int32_t* tok, const int32_t* parent, const int32_t* draft,
+                   int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens, int32_t* bonus,
+                   int32_t* dev_error, hipStream_t stream) {
+  if (N <= 64)
+    hipLaunchKernelGGL(argmax_accept_wave_kernel, dim3(1), dim3(64), 0, stream, N, chunks, part, tok, parent, draft,
+                       accept_len, accept_nodes, accept_tokens, bonus, dev_error);
+  else
+    hipLaunchKernelGGL(argmax_accept_kernel, dim3(1), dim3(kBlock), 0, stream, N, chunks, part, tok, parent, draft,
+                       accept_len, accept_nodes, accept_tokens, bonus, dev_error);
+}
+
 }  // namespace
 
 ArgmaxPlan argmax_plan(int N, int V, int dtype, bool vec) {
@@ -441,8 +485,8 @@ hipError_t launch_argmax_accept(const void* logits, int dtype, int N, int V, int
   uint64_t* part = static_cast<uint64_t*>(workspace);
   hipError_t e = launch_argmax_partial(logits, dtype, N, V, row_bytes, vec, p, tok, part, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(argmax_accept_kernel, dim3(1), dim3(kBlock), 0, stream, N, p.chunks, part, tok, parent, draft,
-                     accept_len, accept_nodes, accept_tokens, bonus, dev_error);
+  launch_finish(N, p.chunks, part, tok, parent, draft, accept_len, accept_nodes, accept_tokens, bonus, dev_error,
+                stream);
   return hipGetLastError();
 }
 
@@ -476,8 +520,8 @@ hipError_t launch_sample_accept(const void* logits, int dtype, int N, int V, int
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(argmax_accept_kernel, dim3(1), dim3(kBlock), 0, stream, N, p.chunks, part, tok, parent, draft,
-                     accept_len, accept_nodes, accept_tokens, bonus, dev_error);
+  launch_finish(N, p.chunks, part, tok, parent, draft, accept_len, accept_nodes, accept_tokens, bonus, dev_error,
+                stream);
   return hipGetLastError();
 }
 

@@ -5,6 +5,7 @@
 // 4742660, "What is DFlash?"); on a DDTree the kept tokens form a root-to-node path
 // (Lucebox-Hub review, aichain-blog.pages.dev, "2. DFlash"). The longest such path wins,
 // ties to the lowest end index.
+#include "tv_accept_wave.h"
 #include "tv_internal.h"
 
 namespace tv {
@@ -50,6 +51,20 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(const int32_t* __restric
   accept_block<kBlock>(anc, par, tok, draft_i, N, okw, red, accept_len, accept_nodes, accept_tokens, bonus);
 }
 
+// At most 64 nodes: one wave, no LDS and no barrier.
+__global__ __launch_bounds__(64) void accept_wave_kernel(const int32_t* __restrict__ parent,
+                                                         const int32_t* __restrict__ draft,
+                                                         const int32_t* __restrict__ tok, int N,
+                                                         int32_t* __restrict__ accept_len,
+                                                         int32_t* __restrict__ accept_nodes,
+                                                         int32_t* __restrict__ accept_tokens,
+                                                         int32_t* __restrict__ bonus, int32_t* dev_error) {
+  const int i = threadIdx.x;
+  const bool valid = i < N;
+  accept_wave(valid ? parent[i] : -1, valid ? draft[i] : 0, valid ? tok[i] : 0, N, accept_len, accept_nodes,
+              accept_tokens, bonus, dev_error);
+}
+
 }  // namespace
 
 hipError_t launch_tree_prep(const int32_t* parent, int N, uint64_t* anc, int32_t* depth,
@@ -62,8 +77,12 @@ hipError_t launch_tree_prep(const int32_t* parent, int N, uint64_t* anc, int32_t
 hipError_t launch_accept(const int32_t* parent, const int32_t* draft, const int32_t* tok, int N,
                          int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
                          int32_t* bonus, int32_t* dev_error, hipStream_t stream) {
-  hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(kBlock), 0, stream, parent, draft, tok, N,
-                     accept_len, accept_nodes, accept_tokens, bonus, dev_error);
+  if (N <= 64)
+    hipLaunchKernelGGL(accept_wave_kernel, dim3(1), dim3(64), 0, stream, parent, draft, tok, N, accept_len,
+                       accept_nodes, accept_tokens, bonus, dev_error);
+  else
+    hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(kBlock), 0, stream, parent, draft, tok, N,
+                       accept_len, accept_nodes, accept_tokens, bonus, dev_error);
   return hipGetLastError();
 }
 
