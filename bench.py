@@ -188,7 +188,72 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="force the KV split count (0 = library choice)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one device copy of this many MiB (counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the bench line: time tv_tree_attn over the bf16, FP8 and 4-bit caches "
+                         "at every workload configuration, one JSON line each")
     return ap.parse_args()
+
+
+def sweep(tv, make, np, torch, dev):
+    """Per-configuration attention times: for each workload, distinct KV buffers (at least
+    8 and 8 GB of bf16 cache, at most 64) in turn, back to back, HIP events; the median of
+    five rounds. The FP8 and 4-bit caches are the same buffers quantised on the GPU."""
+    from workloads import CONFIGS
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    stream = torch.cuda.current_stream()
+    for name in ("tiny_chain", "budget22", "branch_8k", "long_128k", "max_256k", "wide_tree", "decode_1node"):
+        w = make(name, 0, parts=("tree", "qkv"))
+        N, L, Hq, Hkv, D = w.N, w.L, w.Hq, w.Hkv, w.D
+        T, M = L + N, (Hq // Hkv) * N
+        per = 2 * T * Hkv * D * 2
+        nb = int(min(64, max(8, -(-8e9 // per))))
+        K = torch.empty((nb, T, Hkv, D), dtype=torch.bfloat16, device=dev)
+        Vc = torch.empty_like(K)
+        g = torch.Generator(device=dev)
+        g.manual_seed(42)
+        K.normal_(generator=g)
+        Vc.normal_(generator=g)
+        K[0].copy_(to_dev(w.k))
+        Vc[0].copy_(to_dev(w.v))
+        q = to_dev(w.q)
+        parent = torch.from_numpy(w.parent).to(dev)
+        out = torch.empty((N, Hq, D), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(tv.tree_attn_workspace_size(N, L, Hq, Hkv, D), dtype=torch.uint8, device=dev)
+        f8 = [(tv.kv_quantize_fp8(K[b]), tv.kv_quantize_fp8(Vc[b])) for b in range(nb)]
+        f4 = [(tv.kv_quantize_mx4(K[b]), tv.kv_quantize_mx4(Vc[b])) for b in range(nb)]
+        calls = {
+            "bf16": lambda b: tv.tree_attn(q, K[b], Vc[b], parent, L=L, scale=w.scale, out=out, workspace=ws),
+            "fp8": lambda b: tv.tree_attn_fp8(q, f8[b][0][0], f8[b][1][0], f8[b][0][1], f8[b][1][1], parent, L=L,
+                                              scale=w.scale, out=out, workspace=ws),
+            "mx4": lambda b: tv.tree_attn_mx4(q, f4[b][0][0], f4[b][1][0], f4[b][0][1], f4[b][1][1], parent, L=L,
+                                              scale=w.scale, out=out, workspace=ws),
+        }
+        kv_bytes = {"bf16": 2 * T * Hkv * D * 2, "fp8": 2 * T * Hkv * (D + 4), "mx4": 2 * T * Hkv * (D // 2 + 4)}
+        reps = max(40, nb)
+        rec = {"sweep": name, "L": L, "N": N, "Hq": Hq, "Hkv": Hkv, "rows_per_kv_head": M, "kv_buffers": nb}
+        for fmt, call in calls.items():
+            for b in range(2 * nb):
+                call(b % nb)
+            torch.cuda.synchronize()
+            rounds = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for b in range(reps):
+                    call(b % nb)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                rounds.append(e0.elapsed_time(e1) * 1e3 / reps)
+            t = float(np.median(rounds))
+            rec[f"{fmt}_us"] = round(t, 2)
+            rec[f"{fmt}_kv_tbps"] = round(kv_bytes[fmt] / t / 1e6, 3)
+        rec["bf16_tflops"] = round(4.0 * N * Hq * T * D / rec["bf16_us"] / 1e6, 1)
+        print(json.dumps(rec), flush=True)
+        del K, Vc, f8, f4, calls
+        torch.cuda.empty_cache()
 
 
 def log(msg):
@@ -211,6 +276,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tv.lib()
+    if args.sweep:
+        sweep(tv, make, np, torch, dev)
+        return
 
     log("generating the seeded workload (CPU)")
     w = make(args.workload, 0)
