@@ -24,3 +24,23 @@ def test_multi_rank_launch_is_refused():
     r = _run([], {"WORLD_SIZE": "8"})
     assert r.returncode == 2
     assert "exactly one GPU" in r.stderr
+
+
+def test_sweep_flag_is_parsed():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_cli_probe", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    argv = sys.argv
+    try:
+        sys.argv = ["bench.py", "--sweep"]
+        assert bench.parse().sweep
+        sys.argv = ["bench.py"]
+        assert not bench.parse().sweep
+    finally:
+        sys.argv = argv
+
+
+def test_sweep_refuses_more_than_one_gpu_too():
+    r = _run(["--sweep", "--gpus", "2"])
+    assert r.returncode == 2 and r.stdout == ""
