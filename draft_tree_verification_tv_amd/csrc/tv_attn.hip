@@ -144,17 +144,34 @@ __device__ __forceinline__ int swz_v(int r) { return (0xCA60 >> ((r & 3) * 4)) &
 // flight; completion is tracked by vmcnt. M0 carries the LDS address and is restored.
 // An LDS-DMA load that follows an SALU write of M0 needs one wait state (s_nop 0), or
 // it may still see the previous M0 and write the wrong LDS block.
+// kStream: the cache is streamed, each K/V byte read once per call (or by the few
+// row-tile workgroups of one split), so the copy carries the non-temporal hint at device
+// scope (sc1 nt) and does not displace other data in the caches. Only for copies whose
+// rows cover whole 128-byte lines (bf16 rows of 256 bytes, FP8 rows of 128): a copy of
+// part of a line would drop the line that the neighbouring head's workgroup reads next.
+template <bool kStream>
 __device__ __forceinline__ void dma16(uint32_t lds, uint32_t goff, const void* gbase) {
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %3\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(goff), "s"(gbase)
-      : "memory");
+  if constexpr (kStream)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3 sc1 nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(goff), "s"(gbase)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(goff), "s"(gbase)
+        : "memory");
 }
 
 // The same with 4 bytes per lane (lane i lands at lds + 4*i).
@@ -310,8 +327,8 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
 #pragma unroll
       for (int j = 0; j < BPW; ++j) {
         const uint32_t blk = (uint32_t)((wave + j * NW) * 1024);
-        dma16(raw + blk, base + dk[j], kb8);
-        dma16(raw + F8_TILE_B + blk, base + dv[j], vb8);
+        dma16<true>(raw + blk, base + dk[j], kb8);
+        dma16<true>(raw + F8_TILE_B + blk, base + dv[j], vb8);
       }
     } else {
 #pragma unroll
@@ -319,8 +336,8 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
         const int row = 8 * (wave + j * NW) + (lane >> 3);
         const uint32_t off = (uint32_t)min(kt0 + row, p.T - 1) * rowstride_b + (uint32_t)((lane & 7) << 4);
         const uint32_t blk = (uint32_t)((wave + j * NW) * 1024);
-        dma16(raw + blk, off, kb8);
-        dma16(raw + F8_TILE_B + blk, off, vb8);
+        dma16<true>(raw + blk, off, kb8);
+        dma16<true>(raw + F8_TILE_B + blk, off, vb8);
       }
     }
     if (lane < EPW) {
@@ -337,8 +354,8 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
 #pragma unroll
       for (int j = 0; j < BPW; ++j) {
         const uint32_t blk = (uint32_t)((wave + j * NW) * 1024);
-        dma16(st_lds + blk, base + dk[j], kb8);
-        dma16(st_lds + V_OFF + blk, base + dv[j], vb8);
+        dma16<true>(st_lds + blk, base + dk[j], kb8);
+        dma16<true>(st_lds + V_OFF + blk, base + dv[j], vb8);
       }
     } else {
       // Last tile of the sequence: rows past L+N re-read row L+N-1 (always masked).
@@ -348,8 +365,8 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
         const int pc = lane & 15;
         const uint32_t grow = (uint32_t)min(kt0 + row, p.T - 1) * rowstride_b;
         const uint32_t blk = (uint32_t)((wave + j * NW) * 1024);
-        dma16(st_lds + blk, grow + (uint32_t)((pc ^ swz_k(row)) << 4), kb8);
-        dma16(st_lds + V_OFF + blk, grow + (uint32_t)((pc ^ swz_v(row)) << 4), vb8);
+        dma16<true>(st_lds + blk, grow + (uint32_t)((pc ^ swz_k(row)) << 4), kb8);
+        dma16<true>(st_lds + V_OFF + blk, grow + (uint32_t)((pc ^ swz_v(row)) << 4), vb8);
       }
     }
   };
@@ -363,7 +380,7 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
     const uint32_t raw = lds_base + (uint32_t)((t & (F8_NRAW - 1)) * F8_RAW_B);
     const int row = 16 * (wave & 3) + (lane >> 2);
     const uint32_t off = (uint32_t)min(kt0 + row, p.T - 1) * rowstride_b + (uint32_t)((lane & 3) << 4);
-    dma16(raw + (uint32_t)((wave >> 2) * MX_TILE_B + (wave & 3) * 1024), off, cbase);
+    dma16<false>(raw + (uint32_t)((wave >> 2) * MX_TILE_B + (wave & 3) * 1024), off, cbase);
     if (lane < EPW) {
       const uint32_t key = (uint32_t)min(kt0 + ekey, p.T - 1);
       dma4(raw + 2 * MX_TILE_B + wave * EPW * 4, (key * (uint32_t)p.Hkv + (uint32_t)h) * 4u, ebase);
@@ -853,7 +870,7 @@ __global__ __launch_bounds__(RWV * KSW * 64) void attn_split_kernel(SplitParams 
         const int r = 4 * j + (lane >> 4);
         const int pc = lane & 15;
         const uint32_t grow = (uint32_t)min(kbeg + b * 32 + r, p.T - 1) * rowstride_b;
-        dma16(vpriv + (uint32_t)(stage * VB + j * 1024), grow + (uint32_t)((pc ^ swz_v(r)) << 4), vb8);
+        dma16<true>(vpriv + (uint32_t)(stage * VB + j * 1024), grow + (uint32_t)((pc ^ swz_v(r)) << 4), vb8);
       }
     };
     auto compute_block = [&](int b, const bf16x8(&kf)[8], int stage) __attribute__((always_inline)) {
@@ -1179,7 +1196,7 @@ __global__ __launch_bounds__(512) void attn_rows16_kernel(SplitParams p) {
       const int r = 4 * j + (lane >> 4);
       const int pc = lane & 15;
       const uint32_t grow = (uint32_t)min(kbeg + b * 32 + r, p.T - 1) * rowstride_b;
-      dma16(vpriv + (uint32_t)(stage * R16_VB + j * 1024), grow + (uint32_t)((pc ^ swz_v16(r)) << 4), vb8);
+      dma16<true>(vpriv + (uint32_t)(stage * R16_VB + j * 1024), grow + (uint32_t)((pc ^ swz_v16(r)) << 4), vb8);
     }
   };
 
