@@ -45,10 +45,10 @@ CPU_SAMPLE_SECONDS = 10.0
 # profiles/tv_tree_attn_long_128k_hbm_counters.md. Valid only for the kernel sources they
 # were taken on (compared through a digest of their code without comments): reported as
 # null once that code changes.
-TRAFFIC_BYTES_PER_CALL = 572948442
+TRAFFIC_BYTES_PER_CALL = 572862499
 TRAFFIC_SOURCES = ("draft_tree_verification_tv_amd/csrc/tv_attn.hip",
                    "draft_tree_verification_tv_amd/csrc/tv_internal.h")
-TRAFFIC_SOURCES_SHA256 = "6f28b838ad2918a1cfab386065851fe34eb4f2a180c6492e4c6d789037ec2981"
+TRAFFIC_SOURCES_SHA256 = "9a5c140e7d1e013ce8150203dac1510086cc6afb7a068d1ae4b33d9e54cee689"
 
 
 def code_digest(root, files):

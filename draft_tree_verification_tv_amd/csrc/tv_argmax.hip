@@ -90,7 +90,8 @@ __device__ __forceinline__ Best slice_scan(const char* __restrict__ rp, int begi
       for (int u = 0; u < kUnroll; ++u) {
         const int e = begin + (u * kBlock + tid) * EPV;
         const int ea = (e + EPV <= end) ? e : begin;  // clamped: always a full vector in the slice
-        raw[u] = *reinterpret_cast<const u32x4*>(rp + (int64_t)ea * ESZ);
+        // the logits are read once: each wave's load covers 1 KB of whole lines, streamed
+        raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + (int64_t)ea * ESZ));
       }
       int bu = -1;
 #pragma unroll

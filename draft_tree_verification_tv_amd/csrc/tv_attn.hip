@@ -1549,7 +1549,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams mp) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
           const int sj = s0 + min(j + u, cnt - 1);
-          x[u] = __builtin_convertvector(*reinterpret_cast<const bf16x2*>(o_p + (int64_t)sj * TILE_ROWS * D), f32x2);
+          x[u] = __builtin_convertvector(
+              __builtin_nontemporal_load(reinterpret_cast<const bf16x2*>(o_p + (int64_t)sj * TILE_ROWS * D)), f32x2);
         }
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
@@ -1589,8 +1590,9 @@ __global__ __launch_bounds__(256) void attn_merge_small_kernel(MergeParams mp) {
   f32x2 x[NB * 16];
 #pragma unroll
   for (int u = 0; u < NB * 16; ++u)
-    x[u] = __builtin_convertvector(*reinterpret_cast<const bf16x2*>(o_p + (int64_t)min(u, S - 1) * TILE_ROWS * D),
-                                   f32x2);
+    x[u] = __builtin_convertvector(
+        __builtin_nontemporal_load(reinterpret_cast<const bf16x2*>(o_p + (int64_t)min(u, S - 1) * TILE_ROWS * D)),
+        f32x2);
 
   float mx = l;
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));

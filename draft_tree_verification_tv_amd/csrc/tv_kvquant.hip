@@ -28,7 +28,9 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float y0, float y1, float y2, flo
 }
 
 // Rows per 16-lane group in both quantisers: all of a group's loads are issued before any
-// row is converted, so each lane keeps that many 16-byte loads in flight.
+// row is converted, so each lane keeps that many 16-byte loads in flight. Source and codes
+// are streamed (each load and store instruction covers whole 128-byte lines), so both
+// carry the non-temporal hint.
 constexpr int kQuantRows = 4;
 
 // Row (token, head) index -> its element offset in the source and byte offset in the codes;
@@ -55,7 +57,9 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __rest
   for (int r = 0; r < kQuantRows; ++r) {
     const uint32_t row = row0 + 16u * r;
     w[r] = u32x4{0u, 0u, 0u, 0u};
-    if (row < rows) w[r] = *reinterpret_cast<const u32x4*>(src + row_at(row, H, st, sh, 0, 0).src + 8 * sub);
+    if (row < rows)
+      w[r] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(src + row_at(row, H, st, sh, 0, 0).src + 8 * sub));
   }
 #pragma unroll
   for (int r = 0; r < kQuantRows; ++r) {
@@ -82,7 +86,9 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __rest
     for (int j = 0; j < 8; ++j) y[j] = ldexpf(x[j], -e);  // exact: a power-of-two scaling
     const uint32_t lo = e4m3_pack4(y[0], y[1], y[2], y[3]);
     const uint32_t hi = e4m3_pack4(y[4], y[5], y[6], y[7]);
-    *reinterpret_cast<uint2*>(codes + row_at(row, H, 0, 0, cst, csh).codes + 8 * sub) = make_uint2(lo, hi);
+    typedef uint32_t n32x2 __attribute__((ext_vector_type(2)));
+    __builtin_nontemporal_store(n32x2{lo, hi},
+                                reinterpret_cast<n32x2*>(codes + row_at(row, H, 0, 0, cst, csh).codes + 8 * sub));
     if (sub == 0) exps[row] = e;
   }
 }
@@ -130,7 +136,9 @@ __global__ __launch_bounds__(256) void kv_quantize_mx4_kernel(const uint16_t* __
   for (int r = 0; r < kQuantRows; ++r) {
     const uint32_t row = row0 + 16u * r;
     w[r] = u32x4{0u, 0u, 0u, 0u};
-    if (row < rows) w[r] = *reinterpret_cast<const u32x4*>(src + row_at(row, H, st, sh, 0, 0).src + 8 * sub);
+    if (row < rows)
+      w[r] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(src + row_at(row, H, st, sh, 0, 0).src + 8 * sub));
   }
 #pragma unroll
   for (int r = 0; r < kQuantRows; ++r) {
@@ -148,7 +156,8 @@ __global__ __launch_bounds__(256) void kv_quantize_mx4_kernel(const uint16_t* __
       e = min(max(e, kMxExpLo), kMxExpHi);
     }
     const uint32_t c = e2m1_pack8(w[r], __int_as_float((e + 127) << 23));
-    *reinterpret_cast<uint32_t*>(codes + row_at(row, H, 0, 0, cst, csh).codes + 4 * sub) = c;
+    __builtin_nontemporal_store(c,
+                                reinterpret_cast<uint32_t*>(codes + row_at(row, H, 0, 0, cst, csh).codes + 4 * sub));
     if ((sub & 3) == 0) exps[(int64_t)row * 4 + (sub >> 2)] = (int8_t)e;
   }
 }
