@@ -215,7 +215,7 @@ int tv_argmax(const void* logits, int dtype, int N, int V, int64_t row_stride,
  *   accept_tokens  int32 [N]: draft tokens of those nodes, then -1 padding.
  *   bonus          optional int32 [1]: tok of the lowest-index child of the path's last
  *                  node (of the prefix when nothing is accepted), -1 if it has none.
- * Limits: 1 <= N <= TV_MAX_NODES. Runs as a single workgroup.
+ * Limits: 1 <= N <= TV_MAX_NODES. Runs as a single workgroup (a single wave for N <= 64).
  */
 int tv_accept(const int32_t* parent, const int32_t* draft, const int32_t* tok, int N,
               int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
@@ -225,8 +225,9 @@ int tv_accept(const int32_t* parent, const int32_t* draft, const int32_t* tok, i
  * Argmax and acceptance in one call: tok = row argmax of the logits (exactly as
  * tv_argmax), then the longest accepted path on those tokens (exactly as tv_accept). Both
  * steps of greedy verification follow the passages cited for tv_argmax and tv_accept; one
- * workgroup finishes the row reductions and walks the tree, so the pair costs one launch
- * fewer than two separate calls and tok never leaves the chip before the walk.
+ * workgroup (one wave for N <= 64) finishes the row reductions and walks the tree, so the
+ * pair costs one launch fewer than two separate calls and tok never leaves the chip before
+ * the walk.
  *   logits, dtype, V, row_stride, tok, workspace   as for tv_argmax (same workspace size).
  *   parent, draft, accept_len, accept_nodes, accept_tokens, bonus, dev_error   as for
  *            tv_accept.
