@@ -6,18 +6,19 @@
 
 namespace tv {
 
-// The walk of accept_block (tv_internal.h) for a tree of at most 64 nodes, by one wave with lane i = node i and no
-// LDS or barrier: the ancestor sets come from pointer jumping over register shuffles
-// (round r: anc_i |= anc_jmp(i), jmp(i) = jmp(jmp(i)), every lane reading the values of
-// the previous round), then the rule of accept_block. parent_i, draft_i and tok_i are lane
-// i's entries (ignored for lanes >= N); a parent outside [-1, i-1] is read as -1 and
-// reported, as tree_prep_lds does.
+// Lane src's 64-bit value, as two 32-bit shuffles.
 __device__ __forceinline__ uint64_t shfl_u64(uint64_t x, int src) {
   const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)x, src);
   const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(x >> 32), src);
   return ((uint64_t)hi << 32) | lo;
 }
 
+// The walk of accept_block (tv_internal.h) for a tree of at most 64 nodes, by one wave
+// with lane i = node i and no LDS or barrier: the ancestor sets come from pointer jumping
+// over register shuffles (round r: anc_i |= anc_jmp(i), jmp(i) = jmp(jmp(i)), every lane
+// reading the values of the previous round), then the rule of accept_block. parent_i,
+// draft_i and tok_i are lane i's entries (ignored for lanes >= N); a parent outside
+// [-1, i-1] is read as -1 and reported, as tree_prep_lds does.
 __device__ __forceinline__ void accept_wave(int parent_i, int draft_i, int tok_i, int N, int32_t* accept_len,
                                             int32_t* accept_nodes, int32_t* accept_tokens, int32_t* bonus,
                                             int32_t* dev_error) {
