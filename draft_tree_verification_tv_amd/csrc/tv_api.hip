@@ -29,6 +29,20 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 inline int status_of(hipError_t e) { return e == hipSuccess ? TV_OK : TV_ERR_HIP; }
 
+// Whether the rows (t, h), t < T, h < H, of w units at t * st + h * sh are pairwise
+// disjoint in one of the two layouts accepted for a cache that is written: token-major
+// (the heads of a token side by side, then the next token) or head-major (the tokens of a
+// head side by side, then the next head). Strides are non-negative.
+bool rows_disjoint(int64_t st, int64_t sh, int64_t T, int64_t H, int64_t w) {
+  if (st < 0 || sh < 0) return false;
+  if (T <= 0 || H <= 0 || (T == 1 && H == 1)) return true;
+  if (H == 1) return st >= w;
+  if (T == 1) return sh >= w;
+  const bool token_major = sh >= w && st >= (H - 1) * sh + w;
+  const bool head_major = st >= w && sh >= (T - 1) * st + w;
+  return token_major || head_major;
+}
+
 bool attn_args_ok(int N, int L, int Hq, int Hkv, int num_splits) {
   return N >= 1 && N <= TV_MAX_NODES && L >= 0 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0 &&
          num_splits >= 0 && num_splits <= 1024 && (int64_t)L + N <= INT32_MAX - 64 &&
@@ -236,7 +250,7 @@ int tv_kv_commit(void* k, void* v, int64_t kv_stride_t, int64_t kv_stride_h, int
                  void* stream) {
   if (!k || !v || !accept_len || !accept_nodes) return TV_ERR_INVALID_ARG;
   if (N < 1 || N > TV_MAX_NODES || L < 0 || Hkv < 1 || D < 8 || D % 8 != 0 || D > 4096) return TV_ERR_INVALID_ARG;
-  if (kv_stride_t < (int64_t)Hkv * D || kv_stride_h < D || kv_stride_t % 8 != 0 || kv_stride_h % 8 != 0)
+  if (kv_stride_t % 8 != 0 || kv_stride_h % 8 != 0 || !rows_disjoint(kv_stride_t, kv_stride_h, (int64_t)L + N, Hkv, D))
     return TV_ERR_INVALID_ARG;
   if (!aligned16(k) || !aligned16(v)) return TV_ERR_INVALID_ARG;
   return status_of(tv::launch_kv_commit(k, v, kv_stride_t, kv_stride_h, Hkv, D, L, N, accept_len, accept_nodes,
@@ -266,9 +280,8 @@ int tv_kv_quantize_fp8(const void* src, int64_t src_stride_t, int64_t src_stride
   if (!src || !codes || !exps) return TV_ERR_INVALID_ARG;
   if (T < 0 || Hkv < 1 || (int64_t)T * Hkv > INT32_MAX - 4) return TV_ERR_INVALID_ARG;
   if (D != TV_HEAD_DIM) return TV_ERR_UNSUPPORTED;
-  if (src_stride_t < (int64_t)Hkv * D || src_stride_h < D || src_stride_t % 8 || src_stride_h % 8)
-    return TV_ERR_INVALID_ARG;
-  if (codes_stride_t < (int64_t)Hkv * D || codes_stride_h < D || codes_stride_t % 8 || codes_stride_h % 8)
+  if (src_stride_t < 0 || src_stride_h < 0 || src_stride_t % 8 || src_stride_h % 8) return TV_ERR_INVALID_ARG;
+  if (codes_stride_t % 8 || codes_stride_h % 8 || !rows_disjoint(codes_stride_t, codes_stride_h, T, Hkv, D))
     return TV_ERR_INVALID_ARG;
   if (!aligned16(src) || ((uintptr_t)codes % 8) || ((uintptr_t)exps % 4)) return TV_ERR_INVALID_ARG;
   if (T == 0) return TV_OK;
@@ -281,9 +294,8 @@ int tv_kv_quantize_mx4(const void* src, int64_t src_stride_t, int64_t src_stride
   if (!src || !codes || !exps) return TV_ERR_INVALID_ARG;
   if (T < 0 || Hkv < 1 || (int64_t)T * Hkv > INT32_MAX / 4) return TV_ERR_INVALID_ARG;
   if (D != TV_HEAD_DIM) return TV_ERR_UNSUPPORTED;
-  if (src_stride_t < (int64_t)Hkv * D || src_stride_h < D || src_stride_t % 8 || src_stride_h % 8)
-    return TV_ERR_INVALID_ARG;
-  if (codes_stride_t < (int64_t)Hkv * D / 2 || codes_stride_h < D / 2 || codes_stride_t % 16 || codes_stride_h % 16)
+  if (src_stride_t < 0 || src_stride_h < 0 || src_stride_t % 8 || src_stride_h % 8) return TV_ERR_INVALID_ARG;
+  if (codes_stride_t % 16 || codes_stride_h % 16 || !rows_disjoint(codes_stride_t, codes_stride_h, T, Hkv, D / 2))
     return TV_ERR_INVALID_ARG;
   if (!aligned16(src) || !aligned16(codes)) return TV_ERR_INVALID_ARG;
   if (T == 0) return TV_OK;

@@ -99,9 +99,11 @@ int tv_tree_prep(const int32_t* parent, int N, uint64_t* anc, int32_t* depth,
  *
  *   q        bf16 [N][Hq][D], contiguous, 16-byte aligned.
  *   k, v     bf16; element (t, kvh, d) at base + t*kv_stride_t + kvh*kv_stride_h + d
- *            (strides in elements, multiples of 8; d contiguous; 16-byte aligned base).
- *            Rows t in [0, L) are the context, rows L + i are tree node i's own key and
- *            value. Only rows [0, L + N) are read.
+ *            (strides in elements, non-negative multiples of 8; d contiguous; 16-byte
+ *            aligned base). Token-major ([T][Hkv][D]) and head-major ([Hkv][T][D])
+ *            caches are both served through the strides. Rows t in [0, L) are the
+ *            context, rows L + i are tree node i's own key and value. Only rows
+ *            [0, L + N) are read.
  *   parent   int32 [N] (see conventions).
  *   scale    softmax scale applied to q.k (1/sqrt(D) for standard attention).
  *   num_splits  number of KV splits per (KV head, row tile); 0 = library's choice.
@@ -267,9 +269,13 @@ int tv_sample_accept(const void* logits, int dtype, int N, int V, int64_t row_st
  * the verify pass, move in place to rows L + 0, 1, ... in path order:
  *     for j in [0, *accept_len): row L + j <- row L + accept_nodes[j]   (K and V, all heads)
  * Other rows are not touched; the committed sequence then has length L + *accept_len.
- *   k, v         the cache of tv_tree_attn (same layout; any 2-byte element type; rows
+ *   k, v         the cache of tv_tree_attn (same strides; any 2-byte element type; rows
  *                [0, L + N) valid); modified in place. 16-byte aligned.
- *   kv_stride_t, kv_stride_h, Hkv, D   as for tv_tree_attn (D a multiple of 8, <= 4096).
+ *   kv_stride_t, kv_stride_h, Hkv, D   as for tv_tree_attn (D a multiple of 8, <= 4096),
+ *                with the rows (t, h), t < L + N, pairwise disjoint in a token-major
+ *                (kv_stride_h >= D, kv_stride_t >= (Hkv - 1) * kv_stride_h + D) or a
+ *                head-major (kv_stride_t >= D, kv_stride_h >= (L + N - 1) * kv_stride_t + D)
+ *                layout; TV_ERR_INVALID_ARG otherwise.
  *   accept_len, accept_nodes   device int32, as tv_accept writes them.
  *   new_len      optional int32 [1]: receives L + *accept_len.
  *   dev_error    optional: receives TV_ERR_INVALID_ARG when *accept_len is outside [0, N]
@@ -290,12 +296,15 @@ int tv_kv_commit(void* k, void* v, int64_t kv_stride_t, int64_t kv_stride_h, int
  * mantissa, -0 coded as +0. The row dequantises to decode(code) * 2^e, which is exact in
  * bfloat16.
  *   src          bf16 [T][Hkv][D], strides src_stride_t / src_stride_h in elements
- *                (multiples of 8), D contiguous; 16-byte aligned. Values must be finite.
+ *                (non-negative multiples of 8), D contiguous; 16-byte aligned. Values
+ *                must be finite.
  *   codes        uint8 [T][Hkv][D] out, strides codes_stride_t / codes_stride_h in bytes
- *                (multiples of 8), D contiguous; 8-byte aligned.
+ *                (multiples of 8), D contiguous; 8-byte aligned. Its rows must be pairwise
+ *                disjoint in a token-major or a head-major layout (the rule of
+ *                tv_kv_commit with T rows of D bytes).
  *   exps         int32 [T * Hkv] out (row t * Hkv + h), 4-byte aligned.
  * Limits: T >= 0 (T = 0 enqueues nothing), Hkv >= 1, D = TV_HEAD_DIM (else
- * TV_ERR_UNSUPPORTED), strides at least the packed ones.
+ * TV_ERR_UNSUPPORTED).
  */
 int tv_kv_quantize_fp8(const void* src, int64_t src_stride_t, int64_t src_stride_h, int T,
                        int Hkv, int D, void* codes, int64_t codes_stride_t,
@@ -311,13 +320,16 @@ int tv_kv_quantize_fp8(const void* src, int64_t src_stride_t, int64_t src_stride
  * x * 2^-e, ties to the even code, saturating at 6 (only where e was clamped), -0 coded
  * as +0. The block dequantises to decode(code) * 2^e, which is exact in bfloat16.
  *   src          bf16 [T][Hkv][D], strides src_stride_t / src_stride_h in elements
- *                (multiples of 8), D contiguous; 16-byte aligned. Values must be finite.
+ *                (non-negative multiples of 8), D contiguous; 16-byte aligned. Values
+ *                must be finite.
  *   codes        uint8 [T][Hkv][D / 2] out, two codes per byte (value 2j in the low
  *                nibble of byte j), strides codes_stride_t / codes_stride_h in bytes
- *                (multiples of 16), D / 2 contiguous; 16-byte aligned.
+ *                (multiples of 16), D / 2 contiguous; 16-byte aligned. Its rows must be
+ *                pairwise disjoint in a token-major or a head-major layout (the rule of
+ *                tv_kv_commit with T rows of D / 2 bytes).
  *   exps         int8 [T * Hkv * D / 32] out (block b of row (t, h) at (t * Hkv + h) * 4 + b).
  * Limits: T >= 0 (T = 0 enqueues nothing), Hkv >= 1, D = TV_HEAD_DIM (else
- * TV_ERR_UNSUPPORTED), strides at least the packed ones.
+ * TV_ERR_UNSUPPORTED).
  */
 int tv_kv_quantize_mx4(const void* src, int64_t src_stride_t, int64_t src_stride_h, int T,
                        int Hkv, int D, void* codes, int64_t codes_stride_t,

@@ -207,6 +207,9 @@ def test_argmax_accept_workspace_checks():
     ((FAKE, FAKE, 1020, 128, 8, 128, 100, 16, FAKE, FAKE), 1),
     ((FAKE, FAKE, 1024, 124, 8, 128, 100, 16, FAKE, FAKE), 1),
     ((ctypes.c_void_p(0x10008), FAKE, 1024, 128, 8, 128, 100, 16, FAKE, FAKE), 1),
+    ((FAKE, FAKE, 1024, 256, 8, 128, 100, 16, FAKE, FAKE), 1),    # heads 4-7 overlap the next token
+    ((FAKE, FAKE, 128, 14000, 8, 128, 100, 16, FAKE, FAKE), 1),   # head-major, heads overlap
+    ((FAKE, FAKE, -1024, 128, 8, 128, 100, 16, FAKE, FAKE), 1),
 ])
 def test_kv_commit_rejects(args, status):
     assert tv.lib().tv_kv_commit(*args, None, None, None) == status
@@ -269,6 +272,9 @@ def test_binding_refuses_cpu_tensors():
     ((FAKE, 1024, 128, 10, 8, 128, FAKE, 1024, 128, ctypes.c_void_p(0x10002)), 1),
     ((FAKE, 1 << 40, 128, 1 << 30, 8, 128, FAKE, 1 << 40, 128, FAKE), 1),
     ((FAKE, 1024, 128, 0, 8, 128, FAKE, 1024, 128, FAKE), 0),
+    ((FAKE, 1024, 128, 10, 8, 128, FAKE, 1024, 256, FAKE), 1),   # code heads overlap the next token
+    ((FAKE, 1024, 128, 10, 8, 128, FAKE, 128, 1024, FAKE), 1),   # head-major, heads overlap
+    ((FAKE, -8, 128, 10, 8, 128, FAKE, 1024, 128, FAKE), 1),
 ])
 def test_kv_quantize_rejects(args, status):
     assert tv.lib().tv_kv_quantize_fp8(*args, None) == status
@@ -292,6 +298,8 @@ def test_kv_quantize_rejects(args, status):
     ((FAKE, 1024, 128, 10, 8, 128, ctypes.c_void_p(0x10008), 512, 64, FAKE), 1),
     ((FAKE, 1 << 40, 128, 1 << 30, 8, 128, FAKE, 1 << 40, 64, FAKE), 1),
     ((FAKE, 1024, 128, 0, 8, 128, FAKE, 512, 64, ctypes.c_void_p(0x10003)), 0),
+    ((FAKE, 1024, 128, 10, 8, 128, FAKE, 512, 128, FAKE), 1),    # code heads overlap the next token
+    ((FAKE, 1024, 128, 10, 8, 128, FAKE, 64, 512, FAKE), 1),     # head-major, heads overlap
 ])
 def test_kv_quantize_mx4_rejects(args, status):
     assert tv.lib().tv_kv_quantize_mx4(*args, None) == status

@@ -296,6 +296,33 @@ def test_mx4_attention_strided_cache():
     check_attention(out, ref, label="mx4 strided")
 
 
+@pytest.mark.parametrize("name", ["budget22", "decode_1node"])
+def test_mx4_head_major_cache(name):
+    """A head-major bf16 cache quantised on the GPU into head-major codes ([Hkv, T, D/2]
+    viewed as [T, Hkv, D/2]); the exponents stay [T, Hkv, D/32]. Codes and exponents equal
+    the oracle's, and attention over them matches the oracle on the dequantised cache."""
+    w = make(name, 1)
+    T = w.L + w.N
+    note(f"mx4 head-major {name}")
+    kc, ke = oracle.quantize_kv_mx4(w.k)
+    vc, ve = oracle.quantize_kv_mx4(w.v)
+    dev = []
+    for bits in (w.k, w.v):
+        x = dev_bf16(np.ascontiguousarray(bits.transpose(1, 0, 2))).permute(1, 0, 2)
+        codes = torch.empty((w.Hkv, T, 64), dtype=torch.uint8, device="cuda").permute(1, 0, 2)
+        dev.append(tv.kv_quantize_mx4(x, codes=codes))
+    (kcd, ked), (vcd, ved) = dev
+    torch.cuda.synchronize()
+    assert kcd.stride() == (64, T * 64, 1)
+    for got, want in ((kcd, kc), (vcd, vc)):
+        assert np.array_equal(got.cpu().numpy(), want)
+    for got, want in ((ked, ke), (ved, ve)):
+        assert np.array_equal(got.cpu().numpy(), want)
+    out = tv.tree_attn_mx4(dev_bf16(w.q), kcd, vcd, ked, ved, _dev_i32(w.parent), L=w.L, scale=w.scale)
+    ref, _ = _mx4_ref(w.q, kc, ke, vc, ve, w.parent, w.scale)
+    check_attention(out, ref, label=f"mx4 head-major {name}")
+
+
 # budget22 (88 rows) widens shared tiles; decode (8 rows) widens each wave's own blocks.
 @pytest.mark.parametrize("name", ["budget22", "decode_1node"])
 def test_mx4_attention_out_of_range_exponent_is_reported(name):

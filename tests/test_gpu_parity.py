@@ -330,6 +330,26 @@ def test_attention_strided_cache():
     check_attention(out, ref, label="strided")
 
 
+# One case per kernel: the 16-row kernel (decode), 2x4 (tiny_chain), 4x2 (budget22), 8x1
+# (branch_8k).
+@pytest.mark.parametrize("name,trial", [("decode_1node", 0), ("tiny_chain", 1), ("budget22", 3), ("branch_8k", 2)])
+def test_attention_head_major_cache(name, trial):
+    """K and V stored head-major ([Hkv, T, D]: each head's rows contiguous) and passed as
+    [T, Hkv, D] views with strides (D, T*D): the same kernels, through the strides."""
+    w = make(name, trial)
+    T = w.L + w.N
+    note(f"attention head-major {name} trial {trial}")
+    kh = dev_bf16(np.ascontiguousarray(w.k.transpose(1, 0, 2)))
+    vh = dev_bf16(np.ascontiguousarray(w.v.transpose(1, 0, 2)))
+    k, v = kh.permute(1, 0, 2), vh.permute(1, 0, 2)
+    assert k.stride() == (128, T * 128, 1)
+    lse = torch.empty((w.N, w.Hq), dtype=torch.float32, device="cuda")
+    out = tv.tree_attn(dev_bf16(w.q), k, v, dev_i32(w.parent), L=w.L, scale=w.scale, lse=lse)
+    torch.cuda.synchronize()
+    ref, lref = attn_ref(w)
+    check_attention(out, ref, lse, lref, f"{name} head-major")
+
+
 def test_binding_uses_the_current_stream():
     """A call without an explicit stream runs on torch's current stream. On a side stream
     the query is overwritten behind a spin of several milliseconds, then attention reads
@@ -538,6 +558,29 @@ def test_kv_commit_strided_view_and_chain():
     assert _run_commit(parent, np.zeros(n, np.int32), np.zeros(n, np.int32), k, v, 50, 2) == n
     # nothing accepted: the cache must not change
     assert _run_commit(parent, np.zeros(n, np.int32), np.ones(n, np.int32), k, v, 50, 2) == 0
+
+
+def test_kv_commit_head_major_cache():
+    """A head-major cache ([Hkv, T, D] viewed as [T, Hkv, D]): GPU accept feeding the GPU
+    commit, bit for bit against the oracle; rows past L + N stay untouched."""
+    rng = np.random.default_rng(41)
+    for case, (n, L, hkv, d, chain) in enumerate(((40, 100, 4, 128, False), (33, 70, 8, 128, True),
+                                                 (200, 5, 2, 64, False))):
+        parent, draft, tok, k, v = _commit_case(rng, n, L, hkv, d, chain=chain)
+        note(f"kv_commit head-major case {case}: n={n} L={L} hkv={hkv} d={d}")
+        kh = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 0, 2)).view(np.int16)).cuda()
+        vh = torch.from_numpy(np.ascontiguousarray(v.transpose(1, 0, 2)).view(np.int16)).cuda()
+        kd, vd = kh.permute(1, 0, 2), vh.permute(1, 0, 2)
+        assert kd.stride() == (d, k.shape[0] * d, 1)
+        ln, nodes, _, _ = tv.accept(dev_i32(parent), dev_i32(draft), dev_i32(tok))
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        tv.kv_commit(kd, vd, L, ln, nodes, dev_error=err)
+        torch.cuda.synchronize()
+        m, enodes, _, _ = oracle.accept(parent, draft, tok)
+        ek, ev = oracle.kv_commit(k, v, L, enodes)
+        assert err.item() == 0 and int(ln.item()) == m
+        assert np.array_equal(kh.cpu().numpy().view(np.uint16).transpose(1, 0, 2), ek)
+        assert np.array_equal(vh.cpu().numpy().view(np.uint16).transpose(1, 0, 2), ev)
 
 
 def test_kv_commit_full_size_cache():
