@@ -196,15 +196,17 @@ def parse():
 
 def sweep(tv, make, np, torch, dev):
     """Per-configuration attention times: for each workload, distinct KV buffers (at least
-    8 and 8 GB of bf16 cache, at most 64) in turn, back to back, HIP events; the median of
-    five rounds. The FP8 and 4-bit caches are the same buffers quantised on the GPU."""
-    from workloads import CONFIGS
-
+    8 and 8 GB of bf16 cache, at most 64) in turn, back to back, HIP events. The FP8 and
+    4-bit caches are the same buffers quantised on the GPU. Each format is timed over a
+    token-major cache ([T, Hkv, D]) and over the same cache stored head-major ([Hkv, T, D],
+    passed through the strides; fields *_hm_*). The six (layout, format) pairs are timed in
+    turn within each of five rounds, after a warm-up of every pair; the median round."""
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     stream = torch.cuda.current_stream()
-    for name in ("tiny_chain", "budget22", "branch_8k", "long_128k", "max_256k", "wide_tree", "decode_1node"):
+
+    def one_config(name):
         w = make(name, 0, parts=("tree", "qkv"))
         N, L, Hq, Hkv, D = w.N, w.L, w.Hq, w.Hkv, w.D
         T, M = L + N, (Hq // Hkv) * N
@@ -218,42 +220,64 @@ def sweep(tv, make, np, torch, dev):
         Vc.normal_(generator=g)
         K[0].copy_(to_dev(w.k))
         Vc[0].copy_(to_dev(w.v))
+        # the same values, each head's rows contiguous, as [T, Hkv, D] views
+        Kh = torch.empty((nb, Hkv, T, D), dtype=torch.bfloat16, device=dev)
+        Vh = torch.empty_like(Kh)
+        Kh.copy_(K.permute(0, 2, 1, 3))
+        Vh.copy_(Vc.permute(0, 2, 1, 3))
+        caches = {"": (K, Vc), "_hm": (Kh.permute(0, 2, 1, 3), Vh.permute(0, 2, 1, 3))}
         q = to_dev(w.q)
         parent = torch.from_numpy(w.parent).to(dev)
         out = torch.empty((N, Hq, D), dtype=torch.bfloat16, device=dev)
         ws = torch.empty(tv.tree_attn_workspace_size(N, L, Hq, Hkv, D), dtype=torch.uint8, device=dev)
-        f8 = [(tv.kv_quantize_fp8(K[b]), tv.kv_quantize_fp8(Vc[b])) for b in range(nb)]
-        f4 = [(tv.kv_quantize_mx4(K[b]), tv.kv_quantize_mx4(Vc[b])) for b in range(nb)]
-        calls = {
-            "bf16": lambda b: tv.tree_attn(q, K[b], Vc[b], parent, L=L, scale=w.scale, out=out, workspace=ws),
-            "fp8": lambda b: tv.tree_attn_fp8(q, f8[b][0][0], f8[b][1][0], f8[b][0][1], f8[b][1][1], parent, L=L,
-                                              scale=w.scale, out=out, workspace=ws),
-            "mx4": lambda b: tv.tree_attn_mx4(q, f4[b][0][0], f4[b][1][0], f4[b][0][1], f4[b][1][1], parent, L=L,
-                                              scale=w.scale, out=out, workspace=ws),
-        }
+
+        def codes(tag, width):
+            if tag:
+                return torch.empty((Hkv, T, width), dtype=torch.uint8, device=dev).permute(1, 0, 2)
+            return torch.empty((T, Hkv, width), dtype=torch.uint8, device=dev)
+
+        calls = {}
+        for tag, (kb, vb) in caches.items():
+            f8 = [(tv.kv_quantize_fp8(kb[b], codes=codes(tag, D)), tv.kv_quantize_fp8(vb[b], codes=codes(tag, D)))
+                  for b in range(nb)]
+            f4 = [(tv.kv_quantize_mx4(kb[b], codes=codes(tag, D // 2)),
+                   tv.kv_quantize_mx4(vb[b], codes=codes(tag, D // 2))) for b in range(nb)]
+            calls["bf16" + tag] = lambda b, kb=kb, vb=vb: tv.tree_attn(q, kb[b], vb[b], parent, L=L, scale=w.scale,
+                                                                        out=out, workspace=ws)
+            calls["fp8" + tag] = lambda b, f8=f8: tv.tree_attn_fp8(q, f8[b][0][0], f8[b][1][0], f8[b][0][1],
+                                                                   f8[b][1][1], parent, L=L, scale=w.scale, out=out,
+                                                                   workspace=ws)
+            calls["mx4" + tag] = lambda b, f4=f4: tv.tree_attn_mx4(q, f4[b][0][0], f4[b][1][0], f4[b][0][1],
+                                                                   f4[b][1][1], parent, L=L, scale=w.scale, out=out,
+                                                                   workspace=ws)
         kv_bytes = {"bf16": 2 * T * Hkv * D * 2, "fp8": 2 * T * Hkv * (D + 4), "mx4": 2 * T * Hkv * (D // 2 + 4)}
         reps = max(40, nb)
-        rec = {"sweep": name, "L": L, "N": N, "Hq": Hq, "Hkv": Hkv, "rows_per_kv_head": M, "kv_buffers": nb}
-        for fmt, call in calls.items():
+        for call in calls.values():
             for b in range(2 * nb):
                 call(b % nb)
-            torch.cuda.synchronize()
-            rounds = []
-            for _ in range(5):
+        torch.cuda.synchronize()
+        rounds = {key: [] for key in calls}
+        for r in range(5):
+            # the order of the pairs alternates between rounds
+            for key in (list(calls) if r % 2 == 0 else list(calls)[::-1]):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
                 for b in range(reps):
-                    call(b % nb)
+                    calls[key](b % nb)
                 e1.record(stream)
                 torch.cuda.synchronize()
-                rounds.append(e0.elapsed_time(e1) * 1e3 / reps)
-            t = float(np.median(rounds))
-            rec[f"{fmt}_us"] = round(t, 2)
-            rec[f"{fmt}_kv_tbps"] = round(kv_bytes[fmt] / t / 1e6, 3)
+                rounds[key].append(e0.elapsed_time(e1) * 1e3 / reps)
+        rec = {"sweep": name, "L": L, "N": N, "Hq": Hq, "Hkv": Hkv, "rows_per_kv_head": M, "kv_buffers": nb}
+        for key in calls:
+            t = float(np.median(rounds[key]))
+            rec[f"{key}_us"] = round(t, 2)
+            rec[f"{key}_kv_tbps"] = round(kv_bytes[key.split("_")[0]] / t / 1e6, 3)
         rec["bf16_tflops"] = round(4.0 * N * Hq * T * D / rec["bf16_us"] / 1e6, 1)
-        print(json.dumps(rec), flush=True)
-        del K, Vc, f8, f4, calls
-        torch.cuda.empty_cache()
+        return rec
+
+    for name in ("tiny_chain", "budget22", "branch_8k", "long_128k", "max_256k", "wide_tree", "decode_1node"):
+        print(json.dumps(one_config(name)), flush=True)
+        torch.cuda.empty_cache()  # the configuration's buffers died with one_config
 
 
 def log(msg):
