@@ -195,8 +195,9 @@ def tree_attn_workspace_size(N, L, Hq, Hkv, D=HEAD_DIM, num_splits=0) -> int:
 def tree_attn(q, k, v, parent, L=None, scale=None, num_splits=0, out=None, lse=None,
               workspace=None, dev_error=None, stream=None):
     """Tree-masked attention. q bf16 [N, Hq, D]; k, v bf16 [>= L+N, Hkv, D] (last dim
-    contiguous); parent int32 [N]. Returns out bf16 [N, Hq, D] (and fills ``lse`` fp32
-    [N, Hq] when given)."""
+    contiguous; any strides, e.g. a head-major [Hkv, T, D] cache viewed through
+    permute(1, 0, 2)); parent int32 [N]. Returns out bf16 [N, Hq, D] (and fills ``lse``
+    fp32 [N, Hq] when given)."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need_cuda(name, t, torch.bfloat16)
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
@@ -518,7 +519,8 @@ def sample_accept(logits, parent, draft, temperature, seed, offset=0, tok=None, 
 def kv_commit(k, v, L, accept_len, accept_nodes, N=None, new_len=None, dev_error=None, stream=None):
     """Move the accepted nodes' K/V rows (cache rows L + node) to rows L + 0, 1, ... in path
     order, in place. k, v: [>= L+N, Hkv, D] 2-byte tensors sharing strides (last dim
-    contiguous); accept_len, accept_nodes: int32 device tensors as tv_accept writes them."""
+    contiguous; rows disjoint in a token-major or a head-major layout); accept_len,
+    accept_nodes: int32 device tensors as tv_accept writes them."""
     for name, t in (("k", k), ("v", v)):
         _need_cuda(name, t)
         if t.element_size() != 2 or t.dim() != 3:
