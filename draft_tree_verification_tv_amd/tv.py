@@ -547,13 +547,16 @@ def kv_commit(k, v, L, accept_len, accept_nodes, N=None, new_len=None, dev_error
 def kv_quantize_fp8(x, codes=None, exps=None, stream=None):
     """Quantise a bf16 cache x [T, Hkv, D] (last dim contiguous) to E4M3 codes (uint8,
     same shape) and one power-of-two exponent per (token, head) row (int32 [T, Hkv]); the
-    row dequantises to code * 2^exp. Returns (codes, exps)."""
+    row dequantises to code * 2^exp. Returns (codes, exps). Codes allocated here are
+    stored head-major (each head's rows side by side, returned as the [T, Hkv, D] view),
+    the layout tree attention streams fastest; a caller's codes buffer may be token- or
+    head-major."""
     _need_cuda("x", x, torch.bfloat16)
     if x.dim() != 3 or (x.numel() and x.stride(2) != 1):
         raise ValueError("x must be [T, Hkv, D] with a contiguous last dim")
     T, H, D = x.shape
     if codes is None:
-        codes = torch.empty((T, H, D), dtype=torch.uint8, device=x.device)
+        codes = torch.empty((H, T, D), dtype=torch.uint8, device=x.device).permute(1, 0, 2)
     if exps is None:
         exps = torch.empty((T, H), dtype=torch.int32, device=x.device)
     _need_cuda("codes", codes, torch.uint8)
@@ -573,7 +576,10 @@ def kv_quantize_mx4(x, codes=None, exps=None, stream=None):
     """Quantise a bf16 cache x [T, Hkv, D] (last dim contiguous) to 4-bit E2M1 codes, two
     per byte (uint8 [T, Hkv, D / 2]; value 2j in the low nibble of byte j), and one
     power-of-two exponent per 32-value block (int8 [T, Hkv, D / 32], contiguous); a block
-    dequantises to code * 2^exp. Returns (codes, exps)."""
+    dequantises to code * 2^exp. Returns (codes, exps). Codes allocated here are stored
+    head-major (each head's 64-byte rows side by side, so tree attention reads whole
+    cache lines; returned as the [T, Hkv, D / 2] view); a caller's codes buffer may be
+    token- or head-major."""
     _need_cuda("x", x, torch.bfloat16)
     if x.dim() != 3 or (x.numel() and x.stride(2) != 1):
         raise ValueError("x must be [T, Hkv, D] with a contiguous last dim")
@@ -581,7 +587,7 @@ def kv_quantize_mx4(x, codes=None, exps=None, stream=None):
     if D % 32:
         raise ValueError("D must be a multiple of 32")
     if codes is None:
-        codes = torch.empty((T, H, D // 2), dtype=torch.uint8, device=x.device)
+        codes = torch.empty((H, T, D // 2), dtype=torch.uint8, device=x.device).permute(1, 0, 2)
     if exps is None:
         exps = torch.empty((T, H, D // 32), dtype=torch.int8, device=x.device)
     _need_cuda("codes", codes, torch.uint8)
