@@ -38,8 +38,9 @@ bool rows_disjoint(int64_t st, int64_t sh, int64_t T, int64_t H, int64_t w) {
   if (T <= 0 || H <= 0 || (T == 1 && H == 1)) return true;
   if (H == 1) return st >= w;
   if (T == 1) return sh >= w;
-  const bool token_major = sh >= w && st >= (H - 1) * sh + w;
-  const bool head_major = st >= w && sh >= (T - 1) * st + w;
+  // 128-bit products: no stride or count the caller passes can overflow them
+  const bool token_major = sh >= w && (__int128)st >= (__int128)(H - 1) * sh + w;
+  const bool head_major = st >= w && (__int128)sh >= (__int128)(T - 1) * st + w;
   return token_major || head_major;
 }
 

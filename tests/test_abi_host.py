@@ -210,6 +210,7 @@ def test_argmax_accept_workspace_checks():
     ((FAKE, FAKE, 1024, 256, 8, 128, 100, 16, FAKE, FAKE), 1),    # heads 4-7 overlap the next token
     ((FAKE, FAKE, 128, 14000, 8, 128, 100, 16, FAKE, FAKE), 1),   # head-major, heads overlap
     ((FAKE, FAKE, -1024, 128, 8, 128, 100, 16, FAKE, FAKE), 1),
+    ((FAKE, FAKE, 1 << 62, 1 << 61, 8, 128, 100, 16, FAKE, FAKE), 1),  # (Hkv - 1) * stride_h past 2^63
 ])
 def test_kv_commit_rejects(args, status):
     assert tv.lib().tv_kv_commit(*args, None, None, None) == status
