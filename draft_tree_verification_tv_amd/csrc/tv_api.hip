@@ -62,7 +62,7 @@ int attn_bf16_args_status(const void* q, const void* k, const void* v, int64_t k
   if (kv_stride_t < 0 || kv_stride_h < 0 || kv_stride_t % 8 || kv_stride_h % 8) return TV_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return TV_ERR_INVALID_ARG;
   // One KV head's rows must be addressable with 32-bit byte offsets.
-  if (((int64_t)L + N) * kv_stride_t * 2 + 4096 > (int64_t)UINT32_MAX) return TV_ERR_UNSUPPORTED;
+  if ((__int128)((int64_t)L + N) * kv_stride_t * 2 + 4096 > (__int128)UINT32_MAX) return TV_ERR_UNSUPPORTED;
   return TV_OK;
 }
 
@@ -172,8 +172,8 @@ int tv_tree_attn_fp8(const void* q, const void* k_codes, const void* v_codes, co
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return TV_ERR_INVALID_ARG;
   // One KV head's code rows and the exponent arrays must be addressable with 32-bit
   // byte offsets.
-  if (((int64_t)L + N) * kv_stride_t + 4096 > (int64_t)UINT32_MAX) return TV_ERR_UNSUPPORTED;
-  if (((int64_t)L + N) * Hkv * 4 > (int64_t)UINT32_MAX) return TV_ERR_UNSUPPORTED;
+  if ((__int128)((int64_t)L + N) * kv_stride_t + 4096 > (__int128)UINT32_MAX) return TV_ERR_UNSUPPORTED;
+  if ((__int128)((int64_t)L + N) * Hkv * 4 > (__int128)UINT32_MAX) return TV_ERR_UNSUPPORTED;
   const tv::AttnPlan p = tv::attn_plan(N, L, Hq, Hkv, num_splits, cu_count());
   const size_t need = tv::attn_workspace_bytes(p, Hkv);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return TV_ERR_WORKSPACE;
@@ -197,8 +197,8 @@ int tv_tree_attn_mx4(const void* q, const void* k_codes, const void* v_codes, co
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return TV_ERR_INVALID_ARG;
   // One KV head's code rows and the exponent words must be addressable with 32-bit byte
   // offsets.
-  if (((int64_t)L + N) * kv_stride_t + 4096 > (int64_t)UINT32_MAX) return TV_ERR_UNSUPPORTED;
-  if (((int64_t)L + N) * Hkv * 4 > (int64_t)UINT32_MAX) return TV_ERR_UNSUPPORTED;
+  if ((__int128)((int64_t)L + N) * kv_stride_t + 4096 > (__int128)UINT32_MAX) return TV_ERR_UNSUPPORTED;
+  if ((__int128)((int64_t)L + N) * Hkv * 4 > (__int128)UINT32_MAX) return TV_ERR_UNSUPPORTED;
   const tv::AttnPlan p = tv::attn_plan(N, L, Hq, Hkv, num_splits, cu_count());
   const size_t need = tv::attn_workspace_bytes(p, Hkv);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return TV_ERR_WORKSPACE;
