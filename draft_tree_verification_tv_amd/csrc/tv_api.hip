@@ -44,6 +44,16 @@ bool rows_disjoint(int64_t st, int64_t sh, int64_t T, int64_t H, int64_t w) {
   return token_major || head_major;
 }
 
+// Whether rows x cols entries of w elements of esize bytes, entry (r, c) at element
+// r * st + c * sh (strides non-negative), span at most 2^56 bytes. No real allocation is
+// larger, and every address the kernels form inside such a span stays far from 64-bit
+// overflow.
+bool span_ok(int64_t rows, int64_t st, int64_t cols, int64_t sh, int64_t w, int64_t esize) {
+  if (rows <= 0 || cols <= 0) return true;
+  const __int128 end = (__int128)(rows - 1) * st + (__int128)(cols - 1) * sh + w;
+  return end * esize <= ((__int128)1 << 56);
+}
+
 bool attn_args_ok(int N, int L, int Hq, int Hkv, int num_splits) {
   return N >= 1 && N <= TV_MAX_NODES && L >= 0 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0 &&
          num_splits >= 0 && num_splits <= 1024 && (int64_t)L + N <= INT32_MAX - 64 &&
@@ -60,6 +70,7 @@ int attn_bf16_args_status(const void* q, const void* k, const void* v, int64_t k
   if (!(scale > 0.f) || !std::isfinite(scale)) return TV_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return TV_ERR_INVALID_ARG;
   if (kv_stride_t < 0 || kv_stride_h < 0 || kv_stride_t % 8 || kv_stride_h % 8) return TV_ERR_INVALID_ARG;
+  if (!span_ok((int64_t)L + N, kv_stride_t, Hkv, kv_stride_h, D, 2)) return TV_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return TV_ERR_INVALID_ARG;
   // One KV head's rows must be addressable with 32-bit byte offsets.
   if ((__int128)((int64_t)L + N) * kv_stride_t * 2 + 4096 > (__int128)UINT32_MAX) return TV_ERR_UNSUPPORTED;
@@ -169,6 +180,7 @@ int tv_tree_attn_fp8(const void* q, const void* k_codes, const void* v_codes, co
   if ((reinterpret_cast<uintptr_t>(k_exps) & 3u) || (reinterpret_cast<uintptr_t>(v_exps) & 3u))
     return TV_ERR_INVALID_ARG;
   if (kv_stride_t < 0 || kv_stride_h < 0 || kv_stride_t % 16 || kv_stride_h % 16) return TV_ERR_INVALID_ARG;
+  if (!span_ok((int64_t)L + N, kv_stride_t, Hkv, kv_stride_h, D, 1)) return TV_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return TV_ERR_INVALID_ARG;
   // One KV head's code rows and the exponent arrays must be addressable with 32-bit
   // byte offsets.
@@ -194,6 +206,7 @@ int tv_tree_attn_mx4(const void* q, const void* k_codes, const void* v_codes, co
   if ((reinterpret_cast<uintptr_t>(k_exps) & 3u) || (reinterpret_cast<uintptr_t>(v_exps) & 3u))
     return TV_ERR_INVALID_ARG;
   if (kv_stride_t < 0 || kv_stride_h < 0 || kv_stride_t % 16 || kv_stride_h % 16) return TV_ERR_INVALID_ARG;
+  if (!span_ok((int64_t)L + N, kv_stride_t, Hkv, kv_stride_h, D / 2, 1)) return TV_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return TV_ERR_INVALID_ARG;
   // One KV head's code rows and the exponent words must be addressable with 32-bit byte
   // offsets.
@@ -216,6 +229,7 @@ int tv_argmax(const void* logits, int dtype, int N, int V, int64_t row_stride, i
               size_t workspace_bytes, void* stream) {
   if (!logits || !tok) return TV_ERR_INVALID_ARG;
   if (N < 1 || N > 65535 || V < 1 || V >= INT32_MAX || row_stride < V) return TV_ERR_INVALID_ARG;
+  if (!span_ok(N, row_stride, 1, 0, V, dtype == TV_F32 ? 4 : 2)) return TV_ERR_INVALID_ARG;
   if (dtype != TV_BF16 && dtype != TV_F32) return TV_ERR_INVALID_ARG;
   const size_t need = tv::argmax_workspace_bytes(N, V);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return TV_ERR_WORKSPACE;
@@ -238,6 +252,7 @@ int tv_argmax_accept(const void* logits, int dtype, int N, int V, int64_t row_st
   if (!logits || !tok || !parent || !draft || !accept_len || !accept_nodes || !accept_tokens)
     return TV_ERR_INVALID_ARG;
   if (N < 1 || N > TV_MAX_NODES || V < 1 || V >= INT32_MAX || row_stride < V) return TV_ERR_INVALID_ARG;
+  if (!span_ok(N, row_stride, 1, 0, V, dtype == TV_F32 ? 4 : 2)) return TV_ERR_INVALID_ARG;
   if (dtype != TV_BF16 && dtype != TV_F32) return TV_ERR_INVALID_ARG;
   const size_t need = tv::argmax_workspace_bytes(N, V);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return TV_ERR_WORKSPACE;
@@ -253,6 +268,7 @@ int tv_kv_commit(void* k, void* v, int64_t kv_stride_t, int64_t kv_stride_h, int
   if (N < 1 || N > TV_MAX_NODES || L < 0 || Hkv < 1 || D < 8 || D % 8 != 0 || D > 4096) return TV_ERR_INVALID_ARG;
   if (kv_stride_t % 8 != 0 || kv_stride_h % 8 != 0 || !rows_disjoint(kv_stride_t, kv_stride_h, (int64_t)L + N, Hkv, D))
     return TV_ERR_INVALID_ARG;
+  if (!span_ok((int64_t)L + N, kv_stride_t, Hkv, kv_stride_h, D, 2)) return TV_ERR_INVALID_ARG;
   if (!aligned16(k) || !aligned16(v)) return TV_ERR_INVALID_ARG;
   return status_of(tv::launch_kv_commit(k, v, kv_stride_t, kv_stride_h, Hkv, D, L, N, accept_len, accept_nodes,
                                         new_len, dev_error, static_cast<hipStream_t>(stream)));
@@ -265,6 +281,7 @@ int tv_sample_accept(const void* logits, int dtype, int N, int V, int64_t row_st
   if (!logits || !tok || !parent || !draft || !accept_len || !accept_nodes || !accept_tokens)
     return TV_ERR_INVALID_ARG;
   if (N < 1 || N > TV_MAX_NODES || V < 1 || V >= INT32_MAX - 8 || row_stride < V) return TV_ERR_INVALID_ARG;
+  if (!span_ok(N, row_stride, 1, 0, V, dtype == TV_F32 ? 4 : 2)) return TV_ERR_INVALID_ARG;
   if (dtype != TV_BF16 && dtype != TV_F32) return TV_ERR_INVALID_ARG;
   if (!(temperature > 0.f) || !std::isfinite(temperature) ||
       !std::isfinite((float)(1.4426950408889634 / (double)temperature)))
@@ -284,6 +301,8 @@ int tv_kv_quantize_fp8(const void* src, int64_t src_stride_t, int64_t src_stride
   if (src_stride_t < 0 || src_stride_h < 0 || src_stride_t % 8 || src_stride_h % 8) return TV_ERR_INVALID_ARG;
   if (codes_stride_t % 8 || codes_stride_h % 8 || !rows_disjoint(codes_stride_t, codes_stride_h, T, Hkv, D))
     return TV_ERR_INVALID_ARG;
+  if (!span_ok(T, src_stride_t, Hkv, src_stride_h, D, 2) || !span_ok(T, codes_stride_t, Hkv, codes_stride_h, D, 1))
+    return TV_ERR_INVALID_ARG;
   if (!aligned16(src) || ((uintptr_t)codes % 8) || ((uintptr_t)exps % 4)) return TV_ERR_INVALID_ARG;
   if (T == 0) return TV_OK;
   return status_of(tv::launch_kv_quantize(src, src_stride_t, src_stride_h, T, Hkv, codes, codes_stride_t,
@@ -297,6 +316,8 @@ int tv_kv_quantize_mx4(const void* src, int64_t src_stride_t, int64_t src_stride
   if (D != TV_HEAD_DIM) return TV_ERR_UNSUPPORTED;
   if (src_stride_t < 0 || src_stride_h < 0 || src_stride_t % 8 || src_stride_h % 8) return TV_ERR_INVALID_ARG;
   if (codes_stride_t % 16 || codes_stride_h % 16 || !rows_disjoint(codes_stride_t, codes_stride_h, T, Hkv, D / 2))
+    return TV_ERR_INVALID_ARG;
+  if (!span_ok(T, src_stride_t, Hkv, src_stride_h, D, 2) || !span_ok(T, codes_stride_t, Hkv, codes_stride_h, D / 2, 1))
     return TV_ERR_INVALID_ARG;
   if (!aligned16(src) || !aligned16(codes)) return TV_ERR_INVALID_ARG;
   if (T == 0) return TV_OK;

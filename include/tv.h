@@ -31,7 +31,9 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls only
  *     enqueue work and never synchronise the host; results appear in stream order.
  *   - Every call returns a tv_status. Arguments that the host can check are checked
- *     before anything is enqueued; a failed check enqueues nothing.
+ *     before anything is enqueued; a failed check enqueues nothing. Strides and sizes
+ *     that together describe more than 2^56 bytes of one array (no allocation is that
+ *     large) are refused with TV_ERR_INVALID_ARG.
  *   - A tree is given as parent[N] (int32, device): parent[i] in [-1, i-1], -1 meaning
  *     "child of the committed prefix". Node order is therefore topological. A kernel
  *     that meets an entry outside that range treats it as -1 and, when `dev_error` is

@@ -75,7 +75,8 @@ def attn_call(**kw):
     (dict(scale=float("inf")), 1), (dict(st=1001), 1), (dict(sh=-8), 1),
     (dict(q=ctypes.c_void_p(0x10002)), 1), (dict(splits=-1), 1), (dict(splits=5000), 1),
     (dict(ws=None), 4), (dict(ws_bytes=16), 4), (dict(ws=ctypes.c_void_p(0x10008)), 4),
-    (dict(st=1 << 20, L=1 << 12), 3), (dict(st=1 << 62), 3),   # rows past 32-bit offsets; a product past 2^64
+    (dict(st=1 << 20, L=1 << 12), 3),                          # one head's rows past 32-bit offsets
+    (dict(st=1 << 62), 1), (dict(sh=1 << 60), 1),              # spans no allocation can have
 ])
 def test_tree_attn_rejects(kw, status):
     assert attn_call(**kw) == status
@@ -96,8 +97,8 @@ def attn_fp8_call(**kw):
     (dict(Hq=6, Hkv=4), 1), (dict(D=64), 3), (dict(scale=0.0), 1), (dict(st=200), 1), (dict(sh=8), 1),
     (dict(k=ctypes.c_void_p(0x10008)), 1), (dict(ek=ctypes.c_void_p(0x10002)), 1),
     (dict(ev=ctypes.c_void_p(0x10001)), 1), (dict(lse=ctypes.c_void_p(0x10002)), 1),
-    (dict(st=1 << 20, L=1 << 12), 3), (dict(Hkv=1 << 20, Hq=1 << 20, L=1 << 12), 3), (dict(st=1 << 62), 3),
-    (dict(ws=None), 4), (dict(ws_bytes=16), 4),
+    (dict(st=1 << 20, L=1 << 12), 3), (dict(Hkv=1 << 20, Hq=1 << 20, L=1 << 12), 3), (dict(st=1 << 62), 1),
+    (dict(sh=1 << 60), 1), (dict(ws=None), 4), (dict(ws_bytes=16), 4),
 ])
 def test_tree_attn_fp8_rejects(kw, status):
     assert attn_fp8_call(**kw) == status
@@ -119,8 +120,8 @@ def attn_mx4_call(**kw):
     (dict(k=ctypes.c_void_p(0x10008)), 1), (dict(v=ctypes.c_void_p(0x10004)), 1),
     (dict(ek=ctypes.c_void_p(0x10002)), 1), (dict(ev=ctypes.c_void_p(0x10001)), 1),
     (dict(lse=ctypes.c_void_p(0x10002)), 1),
-    (dict(st=1 << 20, L=1 << 12), 3), (dict(Hkv=1 << 20, Hq=1 << 20, L=1 << 12), 3), (dict(st=1 << 62), 3),
-    (dict(ws=None), 4), (dict(ws_bytes=16), 4),
+    (dict(st=1 << 20, L=1 << 12), 3), (dict(Hkv=1 << 20, Hq=1 << 20, L=1 << 12), 3), (dict(st=1 << 62), 1),
+    (dict(sh=1 << 60), 1), (dict(ws=None), 4), (dict(ws_bytes=16), 4),
 ])
 def test_tree_attn_mx4_rejects(kw, status):
     assert attn_mx4_call(**kw) == status
@@ -148,6 +149,7 @@ def test_workspace_sizes():
     ((FAKE, 0, 4, 100, 99, FAKE, FAKE, 1 << 30), 1),
     ((FAKE, 0, 4, 100, 100, FAKE, None, 1 << 30), 4),
     ((FAKE, 0, 4, 100, 100, FAKE, FAKE, 8), 4),
+    ((FAKE, 0, 4, 100, 1 << 60, FAKE, FAKE, 1 << 30), 1),     # rows no allocation can hold
 ])
 def test_argmax_rejects(args, status):
     assert tv.lib().tv_argmax(*args, None) == status
