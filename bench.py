@@ -17,10 +17,12 @@ float64 CPU oracle on whole verify calls of the same workload (about 10 s of CPU
 aid; the default line is the 128K one). A call whose flops per algorithmic byte exceed the
 ridge point of the two peaks (2.5 PFLOP/s dense bf16 over 8 TB/s, 312.5 flop/B), as for the
 256-node tree, reports an MFMA roofline: 4 * nodes * q heads * keys * head dim flops per
-call against the bf16 peak.
+call against the bf16 peak. ``--kv-layout head`` stores the bf16 caches head-major
+([Hkv, T, D]) instead of token-major; ``--sweep`` times every configuration's attention
+in the three cache formats and both layouts instead of the bench line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
-       [--no-check]
+       [--no-check] [--kv-layout token|head] [--sweep]
 """
 
 from __future__ import annotations
@@ -186,6 +188,10 @@ def parse():
     ap.add_argument("--workload", default=WORKLOAD,
                     help="configuration to time (profiling aid; the reported metric is long_128k's)")
     ap.add_argument("--splits", type=int, default=0, help="force the KV split count (0 = library choice)")
+    ap.add_argument("--kv-layout", choices=("token", "head"), default="token",
+                    help="bf16 KV cache storage: token-major [T, Hkv, D] (default) or head-major [Hkv, T, D], "
+                         "given to the library through the strides (the read-ceiling probes keep the "
+                         "token-major patterns)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one device copy of this many MiB (counter calibration)")
     ap.add_argument("--sweep", action="store_true",
@@ -314,8 +320,14 @@ def main():
 
     layers = args.layers
     log(f"allocating {layers} KV buffers ({2 * layers * T * Hkv * D * 2 / 1e9:.1f} GB)")
-    K = torch.empty((layers, T, Hkv, D), dtype=torch.bfloat16, device=dev)
-    Vc = torch.empty((layers, T, Hkv, D), dtype=torch.bfloat16, device=dev)
+    if args.kv_layout == "head":
+        # each head's rows side by side; K[b] and Vc[b] are [T, Hkv, D] views of the storage
+        K_store = torch.empty((layers, Hkv, T, D), dtype=torch.bfloat16, device=dev)
+        V_store = torch.empty((layers, Hkv, T, D), dtype=torch.bfloat16, device=dev)
+        K, Vc = K_store.permute(0, 2, 1, 3), V_store.permute(0, 2, 1, 3)
+    else:
+        K = K_store = torch.empty((layers, T, Hkv, D), dtype=torch.bfloat16, device=dev)
+        Vc = V_store = torch.empty((layers, T, Hkv, D), dtype=torch.bfloat16, device=dev)
     K[0].copy_(to_dev(w.k))
     Vc[0].copy_(to_dev(w.v))
     g = torch.Generator(device=dev)
@@ -462,7 +474,8 @@ def main():
     copy_gbps = 2 * cp_n / cp_best / 1e9
     del cp_src, cp_dst
 
-    ceilings = measure_ceilings(K, Vc, T, Hkv, D, layers, stream,
+    # the probes read the caches' storage in the token-major patterns whatever the layout
+    ceilings = measure_ceilings(K_store, V_store, T, Hkv, D, layers, stream,
                                 lambda b: tv.tree_attn(q, K[b], Vc[b], parent, L=L, scale=w.scale,
                                                        num_splits=args.splits, out=out, workspace=ws))
 
@@ -491,7 +504,8 @@ def main():
     else:
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic() if args.workload == WORKLOAD else None,
+                    "traffic": (measured_traffic() if args.workload == WORKLOAD and args.kv_layout == "token"
+                                else None),
                     "kernel": "tv_tree_attn (split + merge)", "algorithmic_bytes": algo_bytes,
                     "traffic_unit": "bytes per call"}
     kv_gbps = kv_bytes / (t_attn_us * 1e-6) / 1e9
@@ -582,7 +596,7 @@ def main():
                                 f"[{N},{V}]; {layers} layer-equivalent attention calls on distinct KV buffers + "
                                 f"argmax + accept per step"),
                    "kv_len": L, "nodes": N, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "vocab": V,
-                   "layers_per_step": layers, "parallelism": "none (1 GPU)"},
+                   "layers_per_step": layers, "kv_layout": args.kv_layout, "parallelism": "none (1 GPU)"},
         "breakdown_us": {"attn_per_call": round(t_attn_us, 2), "attn_mean": round(t_attn_mean_us, 2),
                          "attn_calls_timed": int(attn_ms.size), "argmax_accept": round(t_tokens_us, 2),
                          "attn_p10": round(float(np.percentile(attn_ms, 10) * 1e3), 2),

@@ -1,7 +1,9 @@
-"""bench.py's command line: one GPU only, refused before any GPU work (runs on the CPU)."""
+"""bench.py's command line: one GPU only, refused before any GPU work; flags parsed (runs on the CPU)."""
 import os
 import subprocess
 import sys
+
+import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -44,3 +46,21 @@ def test_sweep_flag_is_parsed():
 def test_sweep_refuses_more_than_one_gpu_too():
     r = _run(["--sweep", "--gpus", "2"])
     assert r.returncode == 2 and r.stdout == ""
+
+
+def test_kv_layout_flag_is_parsed():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_cli_probe2", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    argv = sys.argv
+    try:
+        sys.argv = ["bench.py"]
+        assert bench.parse().kv_layout == "token"
+        sys.argv = ["bench.py", "--kv-layout", "head"]
+        assert bench.parse().kv_layout == "head"
+        sys.argv = ["bench.py", "--kv-layout", "diagonal"]
+        with pytest.raises(SystemExit):
+            bench.parse()
+    finally:
+        sys.argv = argv
